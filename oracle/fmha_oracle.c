@@ -345,6 +345,54 @@ int oracle_combine(const double* o_part, const double* lse_part, int num_splits,
   return 0;
 }
 
+/*
+ * Selected rows only: row n is (query token rows_t[n], query head rows_h[n]),
+ * tokens in the packed indexing of q.  out_rows: [nrows][Dv], lse_rows:
+ * [nrows].  A row of a sequence with no keys is left untouched; the same
+ * per-row computation as oracle_attention.
+ */
+int oracle_attention_rows(const void* q, const void* k, const void* v, int dtype,
+                          const int32_t* cu_q, const int32_t* cu_k, int batch,
+                          int seqlen_q, int seqlen_k, int hq, int hkv, int dqk,
+                          int dv, double scale, double q_descale, double k_descale,
+                          double v_descale, int causal, int window_left,
+                          int window_right, const int32_t* rows_t,
+                          const int32_t* rows_h, int nrows, double* out_rows,
+                          double* lse_rows) {
+  problem P = {q, k, v, dtype, cu_q, cu_k, batch, seqlen_q, seqlen_k,
+               hq, hkv, dqk, dv, scale, q_descale, k_descale, v_descale,
+               window_left, fold_causal(causal, window_right)};
+  if (check_problem(&P)) return -1;
+  int max_sk = 0;
+  for (int b = 0; b < batch; ++b) {
+    int sk = seq_len(cu_k, seqlen_k, b);
+    if (sk > max_sk) max_sk = sk;
+  }
+  int err = 0;
+#pragma omp parallel
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(max_sk > 0 ? max_sk : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int n = 0; n < nrows; ++n) {
+      if (!scores) continue;
+      int t = rows_t[n], h = rows_h[n];
+      int b = 0;
+      while (b < batch && seq_start(cu_q, seqlen_q, b) + seq_len(cu_q, seqlen_q, b) <= t) ++b;
+      if (b >= batch || h < 0 || h >= hq) {
+#pragma omp atomic write
+        err = -1;
+        continue;
+      }
+      int sk = seq_len(cu_k, seqlen_k, b);
+      if (sk == 0) continue;
+      int i = t - seq_start(cu_q, seqlen_q, b);
+      attend_row(&P, b, h, i, 0, sk, scores, out_rows + (int64_t)n * dv, lse_rows + n);
+    }
+    free(scores);
+  }
+  return err;
+}
+
 /* Threads the OpenMP runtime will use (1 without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -56,6 +56,12 @@ def _bind(lib):
     lib.oracle_combine.argtypes = [
         c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_int,
         c_int, c_int, c_int, c_void_p, c_void_p]
+    lib.oracle_attention_rows.restype = c_int
+    lib.oracle_attention_rows.argtypes = [
+        c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_int,
+        c_int, c_int, c_int, c_int, c_int, c_double, c_double, c_double,
+        c_double, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
+        c_void_p]
     lib.oracle_decode.restype = None
     lib.oracle_decode.argtypes = [c_void_p, c_int, ctypes.c_int64, c_void_p]
     lib.oracle_num_threads.restype = c_int
@@ -141,6 +147,29 @@ class Oracle:
             int(window[0]), int(window[1]), _ptr(out), _ptr(lse))
         if rc != 0:
             raise ValueError(f"oracle_attention rejected its arguments ({rc})")
+        return out, lse
+
+    def attention_rows(self, q, k, v, dtype, rows_t, rows_h, *, cu_q=None,
+                       cu_k=None, batch=1, scale, q_descale=1.0, k_descale=1.0,
+                       v_descale=1.0, causal=False, window=(-1, -1), fill=np.nan):
+        """Selected rows (token rows_t[n], head rows_h[n]) -> (out [n,Dv], lse [n])."""
+        q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+        cu_q, cu_k = _cu(cu_q), _cu(cu_k)
+        tq, hq, dqk, hkv, dv, batch, sq, sk = self._geometry(
+            q, k, v, cu_q, cu_k, batch, 0, 0)
+        rt = np.ascontiguousarray(np.asarray(rows_t, dtype=np.int32))
+        rh = np.ascontiguousarray(np.asarray(rows_h, dtype=np.int32))
+        n = len(rt)
+        out = np.full((n, dv), fill, dtype=np.float64)
+        lse = np.full((n,), fill, dtype=np.float64)
+        rc = self.lib.oracle_attention_rows(
+            _ptr(q), _ptr(k), _ptr(v), DTYPE_CODE[dtype], _ptr(cu_q), _ptr(cu_k),
+            batch, sq, sk, hq, hkv, dqk, dv, float(scale), float(q_descale),
+            float(k_descale), float(v_descale), int(bool(causal)),
+            int(window[0]), int(window[1]), _ptr(rt), _ptr(rh), n, _ptr(out),
+            _ptr(lse))
+        if rc != 0:
+            raise ValueError(f"oracle_attention_rows rejected its arguments ({rc})")
         return out, lse
 
     def split_attention(self, q, k, v, dtype, *, chunk, split, cu_q=None,

@@ -391,5 +391,28 @@ def check_decoders(o):
     assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
 
 
+def check_rows_driver(o):
+    # The sampled-rows driver locates (sequence, position) from the packed
+    # token index itself: it must reproduce the full result row for row,
+    # leave no-key rows alone, and the full result is pinned above.
+    p = make_problem("rows", dtype="bf16", lens_q=[3, 0, 4, 2], lens_k=[5, 3, 0, 9],
+                     hq=4, hkv=2, dqk=8, dv=8, seed=500, varlen_q=True, varlen_k=True,
+                     causal=True, window=(2, -1))
+    full_o, full_l = run(o, p)
+    tq = sum(p.lens_q)
+    rt = [t for t in range(tq) for h in range(4)]
+    rh = [h for t in range(tq) for h in range(4)]
+    ro, rl = o.attention_rows(raw_bits(p.q), raw_bits(p.k), raw_bits(p.v), p.dtype,
+                              rt, rh, cu_q=p.cu_q, cu_k=p.cu_k, scale=1 / math.sqrt(8),
+                              causal=True, window=(2, -1))
+    for n, (t, h) in enumerate(zip(rt, rh)):
+        if np.isnan(full_l[h, t]):
+            assert np.isnan(rl[n]) and np.isnan(ro[n]).all(), "no-key row written"
+        else:
+            assert_close(ro[n], full_o[t, h], 0.0, f"rows driver O[{t},{h}]")
+            assert_close([rl[n]], [full_l[h, t]], 0.0, f"rows driver LSE[{h},{t}]")
+
+
 ALL_CHECKS = [check_decoders, check_closed_forms, check_bruteforce, check_sdpa,
-              check_split_combine, check_combine_edge, check_invariants]
+              check_split_combine, check_combine_edge, check_invariants,
+              check_rows_driver]

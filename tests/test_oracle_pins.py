@@ -57,6 +57,9 @@ MUTATIONS = [
      "double w = exp(lse_part[((int64_t)s * hq + h) * tq + t] - L);"),
     ("combine_drops_last_split", "int nsb = (sk + chunk - 1) / chunk;",
      "int nsb = sk / chunk;"),
+    ("rows_driver_wrong_sequence",
+     "while (b < batch && seq_start(cu_q, seqlen_q, b) + seq_len(cu_q, seqlen_q, b) <= t) ++b;",
+     "while (b < batch && seq_start(cu_q, seqlen_q, b) + seq_len(cu_q, seqlen_q, b) < t) ++b;"),
     ("e4m3_bias", "v = ldexp(1.0 + (double)m / 8.0, e - 7);",
      "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     ("f16_subnormal_scale", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
