@@ -1,0 +1,28 @@
+// Compiled attention kernel instances for fp8 inputs (generated list;
+// edit here and in the host's selection rules together).
+#include "fmha_fwd_kernel.h"
+
+namespace fmha {
+
+#define FMHA_INST(DQK, DV, NWM, NWK, BN, ID) \
+  {DT_FP8, DQK, DV, NWM, NWK, BN, ID, &launch_fwd<FwdCfg<DT_FP8, DQK, DV, NWM, NWK, BN>>}
+
+static const FwdKernel kTable[] = {
+    FMHA_INST(128, 128, 1, 4, 64, 0),
+    FMHA_INST(128, 128, 2, 2, 64, 1),
+    FMHA_INST(128, 128, 4, 1, 64, 2),
+    FMHA_INST(128, 128, 5, 1, 64, 3),
+    FMHA_INST(128, 128, 8, 1, 64, 4),
+    FMHA_INST(192, 128, 1, 4, 64, 5),
+    FMHA_INST(192, 128, 2, 2, 64, 6),
+    FMHA_INST(192, 128, 4, 1, 64, 7),
+    FMHA_INST(192, 128, 5, 1, 64, 8),
+    FMHA_INST(192, 128, 8, 1, 64, 9),
+};
+
+const FwdKernel* registry_fp8(int* n) {
+  *n = (int)(sizeof(kTable) / sizeof(kTable[0]));
+  return kTable;
+}
+
+}  // namespace fmha

@@ -1,0 +1,500 @@
+// Attention forward kernel for gfx950 (CDNA4): split-KV partials or final
+// output, packed variable-length sequences, GQA row packing, bottom-right
+// causal / sliding-window / residual masks.
+//
+// Method (web pages on split-KV flash attention): the online-softmax forward
+// of flash attention with exp2, split KV across workgroups for short queries
+// ("[Cute,Fwd,Sm100] Support q_stage=1 for inference", description;
+// "[FlyDSL] Enable FP8 FMHA split-K ...", description), packed varlen with
+// per-sequence offsets, tiles past a sequence's end skipped and tail rows not
+// stored ("Adds variable sequence lengths to the Hopper CuTe DSL FMHA
+// example", sections Interface and Implementation).
+//
+// Workgroup = NWM x NWK wavefronts.  The NWM waves own 16 query rows each
+// (rows = (query position, query head of the kv group) pairs, so the heads of
+// one GQA group fill the MFMA M dimension); the NWK waves split every key
+// block between them and are merged through LDS at the end.  Per iteration the
+// workgroup stages NWK*BN keys of K (row-major) and V (transposed) in LDS,
+// with the next block's global loads in flight in registers.
+//
+// MFMA formulation (16x16 tiles, fp32 accumulate):
+//   S^T[key, row] = K[key, :] . Q[row, :]     A = K tile, B = Q^T
+//   O^T[dv, row] += V^T[dv, key] P^T[key, row] A = V^T tile, B = P^T
+// With S^T's lane-major layout (lane%16 = row, lane/16 = key group) each lane
+// owns one query row, so the softmax row statistics never leave the lane
+// group, P^T feeds the second MFMA straight from registers, and the
+// per-row rescale of O^T is lane-local.  Contraction indices are assigned to
+// (lane group, register slot) consistently between the two operands of each
+// MFMA, which is all the instruction requires.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fmha_params.h"
+
+namespace fmha {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// fp8 probabilities are stored as p * 2^8 (exact power of two) to keep small
+// probabilities in e4m3's normal range; divided out in the epilogue.
+constexpr float kFp8PScale = 256.0f;
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<DT_F32> {
+  static constexpr int bytes = 4;
+};
+template <>
+struct Elem<DT_F16> {
+  static constexpr int bytes = 2;
+};
+template <>
+struct Elem<DT_BF16> {
+  static constexpr int bytes = 2;
+};
+template <>
+struct Elem<DT_FP8> {
+  static constexpr int bytes = 1;
+};
+
+// acc += A_chunk * B_chunk over the contraction slots one 16-byte chunk per
+// lane holds (4 fp32, 8 f16/bf16, 16 fp8 values -> 4, 1, 2 MFMAs).
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_chunk(f32x4 acc, u32x4 a, u32x4 b) {
+  if constexpr (DT == DT_F32) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x),
+                                               __builtin_bit_cast(float, b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.y),
+                                               __builtin_bit_cast(float, b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.z),
+                                               __builtin_bit_cast(float, b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.w),
+                                               __builtin_bit_cast(float, b.w), acc, 0, 0, 0);
+  } else if constexpr (DT == DT_F16) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+  } else if constexpr (DT == DT_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  } else {
+    u32x2 a0 = {a.x, a.y}, a1 = {a.z, a.w}, b0 = {b.x, b.y}, b1 = {b.z, b.w};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a0),
+                                                     __builtin_bit_cast(long, b0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a1),
+                                                     __builtin_bit_cast(long, b1), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  _Float16 x = static_cast<_Float16>(a), y = static_cast<_Float16>(b);
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Probabilities of S^T tiles [4c', 4c'+VPL/4) of one lane, packed as the
+// 16-byte B-operand chunk of the P^T x V^T MFMA in the input element type.
+template <int DT>
+__device__ __forceinline__ u32x4 pack_p(const f32x4* p) {
+  u32x4 r;
+  if constexpr (DT == DT_F32) {
+    r.x = __builtin_bit_cast(uint32_t, p[0].x);
+    r.y = __builtin_bit_cast(uint32_t, p[0].y);
+    r.z = __builtin_bit_cast(uint32_t, p[0].z);
+    r.w = __builtin_bit_cast(uint32_t, p[0].w);
+  } else if constexpr (DT == DT_F16) {
+    r.x = pack_f16x2(p[0].x, p[0].y);
+    r.y = pack_f16x2(p[0].z, p[0].w);
+    r.z = pack_f16x2(p[1].x, p[1].y);
+    r.w = pack_f16x2(p[1].z, p[1].w);
+  } else if constexpr (DT == DT_BF16) {
+    r.x = pack_bf16x2(p[0].x, p[0].y);
+    r.y = pack_bf16x2(p[0].z, p[0].w);
+    r.z = pack_bf16x2(p[1].x, p[1].y);
+    r.w = pack_bf16x2(p[1].z, p[1].w);
+  } else {
+    const float s = kFp8PScale;
+    r.x = pack_fp8x4(p[0].x * s, p[0].y * s, p[0].z * s, p[0].w * s);
+    r.y = pack_fp8x4(p[1].x * s, p[1].y * s, p[1].z * s, p[1].w * s);
+    r.z = pack_fp8x4(p[2].x * s, p[2].y * s, p[2].z * s, p[2].w * s);
+    r.w = pack_fp8x4(p[3].x * s, p[3].y * s, p[3].z * s, p[3].w * s);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask));
+}
+
+// Store 4 consecutive outputs (fp32 values) as out_dtype.
+__device__ __forceinline__ void store_out4(char* dst, int out_dtype, f32x4 v) {
+  if (out_dtype == DT_F32) {
+    *(f32x4*)dst = v;
+  } else if (out_dtype == DT_BF16) {
+    u32x2 w = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    *(u32x2*)dst = w;
+  } else {
+    u32x2 w = {pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w)};
+    *(u32x2*)dst = w;
+  }
+}
+
+template <int DT_, int DQK_, int DV_, int NWM_, int NWK_, int BN_>
+struct FwdCfg {
+  static constexpr int DT = DT_;
+  static constexpr int DQK = DQK_;
+  static constexpr int DV = DV_;
+  static constexpr int NWM = NWM_;
+  static constexpr int NWK = NWK_;
+  static constexpr int BN = BN_;
+  static constexpr int BYTES = Elem<DT>::bytes;
+  static constexpr int VPL = 16 / BYTES;          // elements per 16-byte chunk
+  static constexpr int NTHR = 64 * NWM * NWK;
+  static constexpr int SB = NWK * BN;             // keys per iteration
+  static constexpr int NT = BN / 16;              // S^T tiles per wave
+  static constexpr int CQK = DQK * BYTES / 64;    // QK chunks per row
+  static constexpr int CPV = BN / (4 * VPL);      // PV chunks per wave
+  static constexpr int TV = DV / 16;              // O^T tiles
+  static constexpr int KPITCH = DQK * BYTES + 16; // LDS bytes per K row
+  static constexpr int VPITCH = SB * BYTES + 16;  // LDS bytes per V^T row
+  static constexpr int RK = DQK * BYTES / 16;     // 16-byte chunks per K row
+  static constexpr int RV = DV * BYTES / 16;      // 16-byte chunks per V row
+  static constexpr int KCH = (SB * RK + NTHR - 1) / NTHR;
+  static constexpr int VCH = (SB * RV + NTHR - 1) / NTHR;
+  static constexpr int LDS_KV = SB * KPITCH + DV * VPITCH;
+  static constexpr int LDS_MERGE = NWK > 1 ? NWM * NWK * (TV * 64 * 16 + 16 * 8) : 0;
+  static constexpr int LDS = LDS_KV > LDS_MERGE ? LDS_KV : LDS_MERGE;
+  static_assert(DQK * BYTES % 64 == 0, "head_dim_qk bytes must be a multiple of 64");
+  static_assert(DV % 16 == 0 && DV * BYTES % 16 == 0, "head_dim_v must be a multiple of 16");
+  static_assert(BN % (4 * VPL) == 0 && BN % 16 == 0, "key block must cover whole chunks");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// Position of key `kl` (0..BN) of a wave's key block inside its V^T row:
+// lane group g = (kl%16)/4 owns slots [g*BN/4, (g+1)*BN/4) and slot
+// sigma = 4*(kl/16) + kl%4, matching the order of its S^T registers.
+template <int BN>
+__device__ __forceinline__ int vt_pos(int kl) {
+  return ((kl & 15) >> 2) * (BN / 4) + 4 * (kl >> 4) + (kl & 3);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void fmha_fwd_kernel(FwdParams p) {
+  constexpr int DT = C::DT;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* Ks = smem;
+  char* Vt = smem + C::SB * C::KPITCH;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % C::NWM;
+  const int wk = wave / C::NWM;
+  const int lg = lane >> 4;   // lane group (contraction slots)
+  const int lr = lane & 15;   // query row within the wave tile / MFMA column
+
+  // ---- tile decode: split fastest, then kv head, batch, query tile (reversed,
+  // so the heaviest tiles of causal / long sequences are dispatched first)
+  int64_t bid = blockIdx.x;
+  const int S = p.num_splits;
+  const int split = (int)(bid % S);
+  bid /= S;
+  const int hkv = (int)(bid % p.hkv);
+  bid /= p.hkv;
+  const int b = (int)(bid % p.batch);
+  bid /= p.batch;
+  const int qtile = p.num_q_tiles - 1 - (int)bid;
+
+  int q_off, sq, k_off, sk;
+  if (p.cu_q) {
+    q_off = p.cu_q[b];
+    sq = p.cu_q[b + 1] - q_off;
+  } else {
+    q_off = b * p.seqlen_q;
+    sq = p.seqlen_q;
+  }
+  if (p.cu_k) {
+    k_off = p.cu_k[b];
+    sk = p.cu_k[b + 1] - k_off;
+  } else {
+    k_off = b * p.seqlen_k;
+    sk = p.seqlen_k;
+  }
+  const int G = p.group;
+  const int rows = sq * G;
+  const int row0 = qtile * 16 * C::NWM;
+  if (row0 >= rows || sk <= 0) return;  // past the sequence or no keys: rows untouched
+  const int kb = split * p.chunk;
+  if (kb >= sk) return;                 // split beyond this sequence: not read by the combine
+  const int ke = S > 1 ? min(kb + p.chunk, sk) : sk;
+
+  // ---- pointers
+  const char* kbase = p.k + (p.cu_k ? (int64_t)k_off * p.k_st : (int64_t)b * p.k_sb) + (int64_t)hkv * p.k_sh;
+  const char* vbase = p.v + (p.cu_k ? (int64_t)k_off * p.v_st : (int64_t)b * p.v_sb) + (int64_t)hkv * p.v_sh;
+
+  // ---- this lane's query row
+  const int r = row0 + 16 * wm + lr;
+  const bool row_ok = r < rows;
+  const int iq = row_ok ? r / G : 0;
+  const int hq = hkv * G + (row_ok ? r % G : 0);
+
+  float scale_log2 = p.scale_log2;
+  float v_scale = 1.0f;
+  if constexpr (DT == DT_FP8) {
+    if (p.q_descale) scale_log2 *= *p.q_descale;
+    if (p.k_descale) scale_log2 *= *p.k_descale;
+    if (p.v_descale) v_scale = *p.v_descale;
+    v_scale *= 1.0f / kFp8PScale;
+  }
+
+  // Q^T fragment (B operand): chunk c of row r holds elements [(4c+lg)*VPL, +VPL)
+  u32x4 qf[C::CQK];
+  {
+    const char* qrow = p.q + (p.cu_q ? (int64_t)(q_off + iq) * p.q_st : (int64_t)b * p.q_sb + (int64_t)iq * p.q_st) +
+                       (int64_t)hq * p.q_sh;
+#pragma unroll
+    for (int c = 0; c < C::CQK; ++c) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qf[c] = row_ok ? *(const u32x4*)(qrow + (4 * c + lg) * 16) : z;
+    }
+  }
+
+  // ---- key ranges.  Row i may use keys [lo(i), hi(i)] (bottom-right aligned
+  // causal / window), intersected with this split's [kb, ke).
+  const int shift = sk - sq;
+  auto lo_of = [&](int i) { return p.wl >= 0 ? max(i + shift - p.wl, 0) : 0; };
+  auto hi_of = [&](int i) { return p.wr >= 0 ? min(i + shift + p.wr, sk - 1) : sk - 1; };
+  const int last_row = min(row0 + 16 * C::NWM, rows) - 1;
+  const int iq_lo = row0 / G, iq_hi = last_row / G;
+  const int tile_lo = max(kb, lo_of(iq_lo));
+  const int tile_hi = min(ke - 1, hi_of(iq_hi));
+  const int full_lo = max(kb, lo_of(iq_hi));   // blocks inside [full_lo, full_hi]
+  const int full_hi = min(ke - 1, hi_of(iq_lo)); // need no mask for any row
+  const int my_lo = max(kb, lo_of(iq));
+  const int my_hi = min(ke - 1, hi_of(iq));
+  const int j_begin = (tile_lo / C::SB) * C::SB;
+  const int j_end = tile_hi + 1;
+  const int n_iter = j_end > j_begin ? (j_end - j_begin + C::SB - 1) / C::SB : 0;
+
+  // ---- running state (lane-major: one query row per lane)
+  f32x4 acc[C::TV];
+#pragma unroll
+  for (int t = 0; t < C::TV; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max of scaled log2 scores of row r
+  float l_run = 0.f;        // this lane's partial row sum
+
+  u32x4 kreg[C::KCH], vreg[C::VCH];
+  auto load_block = [&](int j0) {
+#pragma unroll
+    for (int n = 0; n < C::KCH; ++n) {
+      const int ch = tid + n * C::NTHR;
+      const int key = ch / C::RK, part = ch % C::RK;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      const bool ok = ch < C::SB * C::RK && j0 + key < ke;
+      kreg[n] = ok ? *(const u32x4*)(kbase + (int64_t)(j0 + key) * p.k_st + part * 16) : z;
+    }
+#pragma unroll
+    for (int n = 0; n < C::VCH; ++n) {
+      const int ch = tid + n * C::NTHR;
+      const int key = ch / C::RV, part = ch % C::RV;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      const bool ok = ch < C::SB * C::RV && j0 + key < ke;
+      vreg[n] = ok ? *(const u32x4*)(vbase + (int64_t)(j0 + key) * p.v_st + part * 16) : z;
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int n = 0; n < C::KCH; ++n) {
+      const int ch = tid + n * C::NTHR;
+      if (ch < C::SB * C::RK) {
+        const int key = ch / C::RK, part = ch % C::RK;
+        *(u32x4*)(Ks + key * C::KPITCH + part * 16) = kreg[n];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < C::VCH; ++n) {
+      const int ch = tid + n * C::NTHR;
+      if (ch < C::SB * C::RV) {
+        const int key = ch / C::RV, part = ch % C::RV;
+        const int kw = key / C::BN, kl = key % C::BN;
+        char* dst = Vt + (part * C::VPL) * C::VPITCH + (kw * C::BN + vt_pos<C::BN>(kl)) * C::BYTES;
+        const u32x4 w = vreg[n];
+        if constexpr (C::BYTES == 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) *(uint32_t*)(dst + e * C::VPITCH) = w[e];
+        } else if constexpr (C::BYTES == 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *(uint16_t*)(dst + e * C::VPITCH) = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            *(uint8_t*)(dst + e * C::VPITCH) = (uint8_t)(w[e >> 2] >> ((e & 3) * 8));
+        }
+      }
+    }
+  };
+
+  if (n_iter > 0) load_block(j_begin);
+  for (int it = 0; it < n_iter; ++it) {
+    const int j0 = j_begin + it * C::SB;
+    if (it > 0) __syncthreads();
+    store_block();
+    __syncthreads();
+    if (it + 1 < n_iter) load_block(j0 + C::SB);
+
+    // S^T tiles of this wave's BN keys
+    const int kw0 = wk * C::BN;
+    f32x4 s[C::NT];
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::CQK; ++c) {
+#pragma unroll
+      for (int u = 0; u < C::NT; ++u) {
+        const u32x4 kf = *(const u32x4*)(Ks + (kw0 + 16 * u + lr) * C::KPITCH + (4 * c + lg) * 16);
+        s[u] = mfma_chunk<DT>(s[u], kf, qf[c]);
+      }
+    }
+    // scale to log2 units and mask; lane holds keys j0 + kw0 + 16u + 4*lg + e
+    const bool full = j0 >= full_lo && j0 + C::SB - 1 <= full_hi;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = s[u][e] * scale_log2;
+        if (!full) {
+          const int j = j0 + kw0 + 16 * u + 4 * lg + e;
+          if (j < my_lo || j > my_hi) x = -INFINITY;
+        }
+        s[u][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = wave_xor_max(mx, 16);
+    mx = wave_xor_max(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float base = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - base);
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = fast_exp2(s[u][e] - base);
+        s[u][e] = pe;
+        rs += pe;
+      }
+    }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < C::TV; ++t) acc[t] *= alpha;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int c = 0; c < C::CPV; ++c) {
+      const u32x4 pf = pack_p<DT>(&s[c * C::VPL / 4]);
+#pragma unroll
+      for (int t = 0; t < C::TV; ++t) {
+        const u32x4 vf = *(const u32x4*)(Vt + (16 * t + lr) * C::VPITCH +
+                                         (kw0 + lg * (C::BN / 4) + c * C::VPL) * C::BYTES);
+        acc[t] = mfma_chunk<DT>(acc[t], vf, pf);
+      }
+    }
+  }
+
+  // ---- epilogue: row sums across the 4 lane groups, then merge the NWK waves
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  float M = m_run, L = l_tot;
+  // with NWK > 1, wave wk finishes the O^T tiles t with t % NWK == wk
+  if constexpr (C::NWK > 1) {
+    __syncthreads();  // K/V staging no longer read
+    float* accbuf = (float*)smem;
+    float* mlbuf = (float*)(smem + C::NWM * C::NWK * C::TV * 64 * 16);
+    const int wslot = wm * C::NWK + wk;
+#pragma unroll
+    for (int t = 0; t < C::TV; ++t) *(f32x4*)(accbuf + ((wslot * C::TV + t) * 64 + lane) * 4) = acc[t];
+    if (lg == 0) {
+      mlbuf[(wslot * 16 + lr) * 2 + 0] = m_run;
+      mlbuf[(wslot * 16 + lr) * 2 + 1] = l_tot;
+    }
+    __syncthreads();
+    float mk[C::NWK], lk[C::NWK];
+    M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < C::NWK; ++k) {
+      mk[k] = mlbuf[((wm * C::NWK + k) * 16 + lr) * 2 + 0];
+      lk[k] = mlbuf[((wm * C::NWK + k) * 16 + lr) * 2 + 1];
+      M = fmaxf(M, mk[k]);
+    }
+    const float Mb = M == -INFINITY ? 0.f : M;
+    L = 0.f;
+    float w[C::NWK];
+#pragma unroll
+    for (int k = 0; k < C::NWK; ++k) {
+      w[k] = fast_exp2(mk[k] - Mb);
+      L += w[k] * lk[k];
+    }
+#pragma unroll
+    for (int t = 0; t < C::TV; ++t) {
+      if (t % C::NWK != wk) continue;
+      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < C::NWK; ++k)
+        o += w[k] * *(const f32x4*)(accbuf + (((wm * C::NWK + k) * C::TV + t) * 64 + lane) * 4);
+      acc[t] = o;
+    }
+  }
+  if (!row_ok) return;
+  const bool live = L > 0.f;
+  const float inv = live ? v_scale / L : 0.f;
+  const float lse_v = live ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  const int dv_lane = 4 * lg;
+  if (S > 1) {
+    const int64_t tglob = (int64_t)q_off + iq;
+    float* op = p.o_part + (((int64_t)split * p.total_q + tglob) * p.hq + hq) * C::DV + dv_lane;
+#pragma unroll
+    for (int t = 0; t < C::TV; ++t)
+      if (t % C::NWK == wk) *(f32x4*)(op + 16 * t) = acc[t] * inv;
+    if (lg == 0 && wk == 0) p.lse_part[((int64_t)split * p.hq + hq) * p.total_q + tglob] = lse_v;
+  } else {
+    char* op = p.o + (p.cu_q ? (int64_t)(q_off + iq) * p.o_st : (int64_t)b * p.o_sb + (int64_t)iq * p.o_st) +
+               (int64_t)hq * p.o_sh;
+    const int ob = p.out_dtype == DT_F32 ? 4 : 2;
+#pragma unroll
+    for (int t = 0; t < C::TV; ++t)
+      if (t % C::NWK == wk) store_out4(op + (16 * t + dv_lane) * ob, p.out_dtype, acc[t] * inv);
+    if (p.lse && lg == 0 && wk == 0) {
+      const int64_t li = p.cu_q ? (int64_t)hq * p.lse_sh + q_off + iq : (int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + iq;
+      p.lse[li] = lse_v;
+    }
+  }
+}
+
+template <class C>
+hipError_t launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL(fmha_fwd_kernel<C>, dim3((uint32_t)grid), dim3(C::NTHR), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fmha

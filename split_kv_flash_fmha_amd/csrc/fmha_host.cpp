@@ -1,0 +1,423 @@
+// Host side of the C ABI: argument checks, default resolution, the automatic
+// split choice, workspace sizing, kernel selection and launches.
+//
+// Everything up to the launch is plain host code that makes no HIP call, so
+// fmha_fwd_check / fmha_num_splits / fmha_fwd_workspace_size run (and are
+// tested) without a GPU.  Checks follow the pages' rule that an unsupported
+// or invalid configuration is refused before any work instead of silently
+// dropping rows ("Adds variable sequence lengths to the Hopper CuTe DSL FMHA
+// example", section Implementation; "[FlyDSL] Enable FP8 FMHA split-K ...",
+// review: an invalid combination raises an error).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/fmha.h"
+#include "fmha_params.h"
+
+namespace fmha {
+namespace {
+
+constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case FMHA_DTYPE_F32: return 4;
+    case FMHA_DTYPE_F16: return 2;
+    case FMHA_DTYPE_BF16: return 2;
+    case FMHA_DTYPE_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+const FwdKernel* registry(int dt, int* n) {
+  switch (dt) {
+    case FMHA_DTYPE_F32: return registry_f32(n);
+    case FMHA_DTYPE_F16: return registry_f16(n);
+    case FMHA_DTYPE_BF16: return registry_bf16(n);
+    case FMHA_DTYPE_FP8_E4M3: return registry_fp8(n);
+    default: *n = 0; return nullptr;
+  }
+}
+
+// Waves per workgroup along rows / keys for a given number of query rows per
+// (sequence, kv head): single-token decode (<= 16 rows, incl. GQA packing)
+// splits each key block over 4 waves; larger row counts stack 16-row waves.
+void pick_shape(int64_t rows, int* nwm, int* nwk) {
+  if (rows <= 16) {
+    *nwm = 1; *nwk = 4;
+  } else if (rows <= 32) {
+    *nwm = 2; *nwk = 2;
+  } else if (rows <= 64) {
+    *nwm = 4; *nwk = 1;
+  } else if (rows <= 80) {
+    *nwm = 5; *nwk = 1;
+  } else {
+    *nwm = 8; *nwk = 1;
+  }
+}
+
+const FwdKernel* find_exact(int dt, int dqk, int dv, int nwm, int nwk) {
+  int n = 0;
+  const FwdKernel* t = registry(dt, &n);
+  for (int i = 0; i < n; ++i)
+    if (t[i].dqk == dqk && t[i].dv == dv && t[i].nwm == nwm && t[i].nwk == nwk) return &t[i];
+  return nullptr;
+}
+
+// Preferred shape first; wide head dims lack the largest row tiles (register
+// budget), so fall back to narrower workgroups that cover fewer rows each.
+const FwdKernel* find_kernel(int dt, int dqk, int dv, int nwm, int nwk) {
+  if (const FwdKernel* k = find_exact(dt, dqk, dv, nwm, nwk)) return k;
+  static const int fallback[][2] = {{5, 1}, {4, 1}, {2, 2}, {1, 4}};
+  for (const auto& f : fallback)
+    if (f[0] < nwm)
+      if (const FwdKernel* k = find_exact(dt, dqk, dv, f[0], f[1])) return k;
+  return nullptr;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+bool stride_ok(int64_t s, int eb) { return s >= 0 && (s * eb) % 16 == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Resolved {
+  fmha_fwd_plan plan;
+  const FwdKernel* kernel;
+  int64_t sq_max, sk_max, total_q, total_k;
+  bool empty;  // nothing to compute
+};
+
+// Automatic split count.  Parallel units of the non-split grid are
+// (sequence, kv head, query tile); when they cannot fill the device the key
+// range is cut so that about kTargetPerCu workgroups per compute unit exist,
+// each streaming at least kMinChunk keys (the split sweeps on the pages show
+// time falling steeply until the grid covers the machine and flattening or
+// rising a little past that point).
+int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num_cus) {
+  constexpr int kTargetPerCu = 4;
+  constexpr int64_t kMinChunk = 256;
+  if (sk_max <= 0) return 1;
+  const int64_t target = (int64_t)kTargetPerCu * num_cus;
+  if (units >= target / 2) return 1;
+  int64_t chunk = (key_work + target - 1) / target;
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  chunk = (chunk + sb - 1) / sb * sb;
+  int64_t s = (sk_max + chunk - 1) / chunk;
+  if (s < 1) s = 1;
+  if (s > FMHA_MAX_SPLITS) s = FMHA_MAX_SPLITS;
+  return (int)s;
+}
+
+int resolve(const fmha_fwd_args* a, bool check_ws, Resolved* r) {
+  if (!a || !r) return FMHA_ERR_INVALID_ARG;
+  memset(r, 0, sizeof(*r));
+  const int eb = elem_bytes(a->in_dtype);
+  if (eb == 0) return FMHA_ERR_INVALID_ARG;
+  const int ob = elem_bytes(a->out_dtype);
+  if (ob == 0 || a->out_dtype == FMHA_DTYPE_FP8_E4M3) return FMHA_ERR_INVALID_ARG;
+  if (a->in_dtype == FMHA_DTYPE_FP8_E4M3) {
+    if (a->out_dtype != FMHA_DTYPE_BF16) return FMHA_ERR_UNSUPPORTED;
+  } else if (a->out_dtype != a->in_dtype) {
+    return FMHA_ERR_UNSUPPORTED;
+  }
+  if (a->batch < 0 || a->num_heads_q <= 0 || a->num_heads_kv <= 0) return FMHA_ERR_INVALID_ARG;
+  if (a->num_heads_q % a->num_heads_kv != 0) return FMHA_ERR_INVALID_ARG;
+  if (a->head_dim_qk <= 0 || a->head_dim_v <= 0) return FMHA_ERR_INVALID_ARG;
+  if (a->window_left < -1 || a->window_right < -1) return FMHA_ERR_INVALID_ARG;
+  if (!(a->softmax_scale >= 0.f) || isinf(a->softmax_scale)) return FMHA_ERR_INVALID_ARG;
+  if (a->num_kv_splits < 0 || a->num_kv_splits > FMHA_MAX_SPLITS) return FMHA_ERR_INVALID_ARG;
+  if (a->num_cus < 0) return FMHA_ERR_INVALID_ARG;
+
+  const bool vq = a->cu_seqlens_q != nullptr, vk = a->cu_seqlens_k != nullptr;
+  if (vq) {
+    if (a->total_q < 0 || a->max_seqlen_q < 0) return FMHA_ERR_INVALID_ARG;
+    if (a->max_seqlen_q > a->total_q) return FMHA_ERR_INVALID_ARG;
+  } else if (a->seqlen_q < 0) {
+    return FMHA_ERR_INVALID_ARG;
+  }
+  if (vk) {
+    if (a->total_k < 0 || a->max_seqlen_k < 0) return FMHA_ERR_INVALID_ARG;
+    if (a->max_seqlen_k > a->total_k) return FMHA_ERR_INVALID_ARG;
+  } else if (a->seqlen_k < 0) {
+    return FMHA_ERR_INVALID_ARG;
+  }
+  r->sq_max = vq ? a->max_seqlen_q : a->seqlen_q;
+  r->sk_max = vk ? a->max_seqlen_k : a->seqlen_k;
+  r->total_q = vq ? a->total_q : (int64_t)a->batch * a->seqlen_q;
+  r->total_k = vk ? a->total_k : (int64_t)a->batch * a->seqlen_k;
+  if (r->total_q >= ((int64_t)1 << 31) || r->total_k >= ((int64_t)1 << 31)) return FMHA_ERR_INVALID_ARG;
+
+  fmha_fwd_plan& pl = r->plan;
+  pl.softmax_scale = a->softmax_scale == 0.f ? (float)(1.0 / sqrt((double)a->head_dim_qk)) : a->softmax_scale;
+  pl.window_left = a->window_left;
+  pl.window_right = a->causal ? 0 : a->window_right;
+
+  const int G = a->num_heads_q / a->num_heads_kv;
+  int nwm = 1, nwk = 4;
+  pick_shape(r->sq_max * G, &nwm, &nwk);
+  const FwdKernel* kern = find_kernel(a->in_dtype, a->head_dim_qk, a->head_dim_v, nwm, nwk);
+  if (!kern) return FMHA_ERR_UNSUPPORTED;
+  r->kernel = kern;
+  pl.kernel_id = a->in_dtype * 1000 + kern->id;
+  pl.rows_per_tile = 16 * kern->nwm;
+  pl.key_block = kern->nwk * kern->bn;
+  const int64_t rows = r->sq_max * G;
+  pl.num_q_tiles = (int32_t)((rows + pl.rows_per_tile - 1) / pl.rows_per_tile);
+
+  r->empty = a->batch == 0 || r->total_q == 0 || r->sq_max == 0;
+  if (!r->empty) {
+    if (!a->q || !a->k || !a->v || !a->out) return FMHA_ERR_INVALID_ARG;
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->out, 16))
+      return FMHA_ERR_INVALID_ARG;
+    if (a->lse && !aligned(a->lse, 4)) return FMHA_ERR_INVALID_ARG;
+    if (!stride_ok(a->q_stride_tok, eb) || !stride_ok(a->q_stride_head, eb) ||
+        !stride_ok(a->k_stride_tok, eb) || !stride_ok(a->k_stride_head, eb) ||
+        !stride_ok(a->v_stride_tok, eb) || !stride_ok(a->v_stride_head, eb) ||
+        !stride_ok(a->o_stride_tok, ob) || !stride_ok(a->o_stride_head, ob))
+      return FMHA_ERR_INVALID_ARG;
+    if (!vq && (!stride_ok(a->q_stride_batch, eb) || !stride_ok(a->o_stride_batch, ob)))
+      return FMHA_ERR_INVALID_ARG;
+    if (!vk && (!stride_ok(a->k_stride_batch, eb) || !stride_ok(a->v_stride_batch, eb)))
+      return FMHA_ERR_INVALID_ARG;
+    if (a->lse && (a->lse_stride_head < 0 || (!vq && a->lse_stride_batch < 0))) return FMHA_ERR_INVALID_ARG;
+  }
+
+  // splits
+  const int num_cus = a->num_cus > 0 ? a->num_cus : 256;
+  const int64_t units = (int64_t)a->batch * a->num_heads_kv * pl.num_q_tiles;
+  int S;
+  if (a->num_kv_splits > 0) {
+    S = a->num_kv_splits;
+  } else {
+    const int64_t key_work = (int64_t)a->num_heads_kv * pl.num_q_tiles * r->total_k;
+    S = auto_splits(units, key_work, r->sk_max, pl.key_block, num_cus);
+  }
+  pl.num_splits = S;
+  if (S > 1) {
+    int64_t chunk = r->sk_max > 0 ? (r->sk_max + S - 1) / S : 1;
+    chunk = (chunk + pl.key_block - 1) / pl.key_block * pl.key_block;
+    pl.split_chunk = (int32_t)chunk;
+    const size_t o_bytes = (size_t)S * (size_t)r->total_q * a->num_heads_q * a->head_dim_v * sizeof(float);
+    const size_t l_bytes = (size_t)S * (size_t)a->num_heads_q * (size_t)r->total_q * sizeof(float);
+    pl.o_part_offset = 0;
+    pl.lse_part_offset = align256(o_bytes);
+    pl.workspace_bytes = pl.lse_part_offset + align256(l_bytes);
+  } else {
+    pl.split_chunk = (int32_t)(r->sk_max > 0 ? r->sk_max : 1);
+    pl.workspace_bytes = 0;
+  }
+  pl.grid_main = r->empty ? 0 : (int64_t)S * units;
+  if (pl.grid_main >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
+  pl.grid_combine = (r->empty || S == 1) ? 0 : ((r->sq_max * a->num_heads_q + 3) / 4) * a->batch;
+  if (pl.grid_combine >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
+  if (check_ws && S > 1 && !r->empty) {
+    if (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < pl.workspace_bytes)
+      return FMHA_ERR_WORKSPACE;
+  }
+  return FMHA_OK;
+}
+
+FwdParams make_params(const fmha_fwd_args* a, const Resolved& r) {
+  const int eb = elem_bytes(a->in_dtype), ob = elem_bytes(a->out_dtype);
+  FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = (const char*)a->q;
+  p.k = (const char*)a->k;
+  p.v = (const char*)a->v;
+  p.o = (char*)a->out;
+  p.lse = a->lse;
+  if (r.plan.num_splits > 1) {
+    p.o_part = (float*)((char*)a->workspace + r.plan.o_part_offset);
+    p.lse_part = (float*)((char*)a->workspace + r.plan.lse_part_offset);
+  }
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  if (a->in_dtype == FMHA_DTYPE_FP8_E4M3) {
+    p.q_descale = a->q_descale;
+    p.k_descale = a->k_descale;
+    p.v_descale = a->v_descale;
+  }
+  p.batch = a->batch;
+  p.seqlen_q = a->seqlen_q;
+  p.seqlen_k = a->seqlen_k;
+  p.total_q = (int32_t)r.total_q;
+  p.hq = a->num_heads_q;
+  p.hkv = a->num_heads_kv;
+  p.group = a->num_heads_q / a->num_heads_kv;
+  p.q_sb = a->q_stride_batch * eb;
+  p.q_st = a->q_stride_tok * eb;
+  p.q_sh = a->q_stride_head * eb;
+  p.k_sb = a->k_stride_batch * eb;
+  p.k_st = a->k_stride_tok * eb;
+  p.k_sh = a->k_stride_head * eb;
+  p.v_sb = a->v_stride_batch * eb;
+  p.v_st = a->v_stride_tok * eb;
+  p.v_sh = a->v_stride_head * eb;
+  p.o_sb = a->o_stride_batch * ob;
+  p.o_st = a->o_stride_tok * ob;
+  p.o_sh = a->o_stride_head * ob;
+  p.lse_sb = a->lse_stride_batch;
+  p.lse_sh = a->lse_stride_head;
+  p.scale_log2 = (float)((double)r.plan.softmax_scale * 1.4426950408889634);
+  p.wl = r.plan.window_left;
+  p.wr = r.plan.window_right;
+  p.num_splits = r.plan.num_splits;
+  p.chunk = r.plan.split_chunk;
+  p.num_q_tiles = r.plan.num_q_tiles;
+  p.out_dtype = a->out_dtype;
+  return p;
+}
+
+CombineParams make_combine(const fmha_fwd_args* a, const Resolved& r) {
+  const int ob = elem_bytes(a->out_dtype);
+  CombineParams c;
+  memset(&c, 0, sizeof(c));
+  c.o_part = (const float*)((const char*)a->workspace + r.plan.o_part_offset);
+  c.lse_part = (const float*)((const char*)a->workspace + r.plan.lse_part_offset);
+  c.o = (char*)a->out;
+  c.lse = a->lse;
+  c.cu_q = a->cu_seqlens_q;
+  c.cu_k = a->cu_seqlens_k;
+  c.batch = a->batch;
+  c.seqlen_q = a->seqlen_q;
+  c.seqlen_k = a->seqlen_k;
+  c.max_seqlen_q = (int32_t)r.sq_max;
+  c.total_q = (int32_t)r.total_q;
+  c.hq = a->num_heads_q;
+  c.dv = a->head_dim_v;
+  c.num_splits = r.plan.num_splits;
+  c.chunk = r.plan.split_chunk;
+  c.o_sb = a->o_stride_batch * ob;
+  c.o_st = a->o_stride_tok * ob;
+  c.o_sh = a->o_stride_head * ob;
+  c.lse_sb = a->lse_stride_batch;
+  c.lse_sh = a->lse_stride_head;
+  c.out_dtype = a->out_dtype;
+  return c;
+}
+
+}  // namespace
+}  // namespace fmha
+
+using namespace fmha;
+
+extern "C" {
+
+const char* fmha_status_str(int status) {
+  switch (status) {
+    case FMHA_OK: return "ok";
+    case FMHA_ERR_INVALID_ARG: return "invalid argument";
+    case FMHA_ERR_UNSUPPORTED: return "unsupported configuration (no compiled kernel)";
+    case FMHA_ERR_WORKSPACE: return "split workspace missing, misaligned or too small";
+    case FMHA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int fmha_fwd_check(const fmha_fwd_args* args, fmha_fwd_plan* plan) {
+  Resolved r;
+  const int st = resolve(args, true, &r);
+  if (st == FMHA_OK && plan) *plan = r.plan;
+  return st;
+}
+
+int fmha_num_splits(const fmha_fwd_args* args, int32_t* splits_out) {
+  if (!splits_out) return FMHA_ERR_INVALID_ARG;
+  Resolved r;
+  const int st = resolve(args, false, &r);
+  if (st == FMHA_OK) *splits_out = r.plan.num_splits;
+  return st;
+}
+
+int fmha_fwd_workspace_size(const fmha_fwd_args* args, size_t* bytes_out) {
+  if (!bytes_out) return FMHA_ERR_INVALID_ARG;
+  Resolved r;
+  const int st = resolve(args, false, &r);
+  if (st == FMHA_OK) *bytes_out = r.plan.workspace_bytes;
+  return st;
+}
+
+int fmha_fwd(const fmha_fwd_args* args, void* stream) {
+  Resolved r;
+  int st = resolve(args, true, &r);
+  if (st != FMHA_OK) return st;
+  if (r.empty || r.plan.grid_main == 0) return FMHA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const FwdParams p = make_params(args, r);
+  if (r.kernel->launch(p, r.plan.grid_main, s) != hipSuccess) return FMHA_ERR_HIP;
+  if (r.plan.num_splits > 1) {
+    const CombineParams c = make_combine(args, r);
+    if (launch_combine(c, s) != hipSuccess) return FMHA_ERR_HIP;
+  }
+  return FMHA_OK;
+}
+
+int fmha_fwd_splitkv_partials(const fmha_fwd_args* args, void* stream) {
+  Resolved r;
+  int st = resolve(args, true, &r);
+  if (st != FMHA_OK) return st;
+  if (r.plan.num_splits <= 1) return FMHA_ERR_INVALID_ARG;
+  if (r.empty || r.plan.grid_main == 0) return FMHA_OK;
+  const FwdParams p = make_params(args, r);
+  if (r.kernel->launch(p, r.plan.grid_main, (hipStream_t)stream) != hipSuccess) return FMHA_ERR_HIP;
+  return FMHA_OK;
+}
+
+int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
+  if (!a) return FMHA_ERR_INVALID_ARG;
+  const int ob = elem_bytes(a->out_dtype);
+  if (ob == 0 || a->out_dtype == FMHA_DTYPE_FP8_E4M3) return FMHA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->num_heads_q <= 0 || a->head_dim_v <= 0 || a->head_dim_v % 2) return FMHA_ERR_INVALID_ARG;
+  if (a->num_splits < 1 || a->num_splits > FMHA_MAX_SPLITS || a->split_chunk < 1) return FMHA_ERR_INVALID_ARG;
+  const bool vq = a->cu_seqlens_q != nullptr;
+  const int64_t sq_max = vq ? a->max_seqlen_q : a->seqlen_q;
+  const int64_t total_q = vq ? a->total_q : (int64_t)a->batch * a->seqlen_q;
+  if (sq_max < 0 || total_q < 0 || (!a->cu_seqlens_k && a->seqlen_k < 0)) return FMHA_ERR_INVALID_ARG;
+  if (vq && a->max_seqlen_q > a->total_q) return FMHA_ERR_INVALID_ARG;
+  if (a->batch == 0 || total_q == 0 || sq_max == 0) return FMHA_OK;
+  if (!a->o_part || !a->lse_part || !a->out) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(a->o_part, 8) || !aligned(a->lse_part, 4) || !aligned(a->out, 2 * ob)) return FMHA_ERR_INVALID_ARG;
+  if (a->lse && !aligned(a->lse, 4)) return FMHA_ERR_INVALID_ARG;
+  if (a->o_stride_tok < 0 || a->o_stride_head < 0 || (a->o_stride_tok * ob) % (2 * ob) ||
+      (a->o_stride_head * ob) % (2 * ob) || (!vq && (a->o_stride_batch < 0 || a->o_stride_batch % 2)))
+    return FMHA_ERR_INVALID_ARG;
+  if ((sq_max * a->num_heads_q + 3) / 4 * a->batch >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
+  CombineParams c;
+  memset(&c, 0, sizeof(c));
+  c.o_part = a->o_part;
+  c.lse_part = a->lse_part;
+  c.o = (char*)a->out;
+  c.lse = a->lse;
+  c.cu_q = a->cu_seqlens_q;
+  c.cu_k = a->cu_seqlens_k;
+  c.batch = a->batch;
+  c.seqlen_q = a->seqlen_q;
+  c.seqlen_k = a->seqlen_k;
+  c.max_seqlen_q = (int32_t)sq_max;
+  c.total_q = (int32_t)total_q;
+  c.hq = a->num_heads_q;
+  c.dv = a->head_dim_v;
+  c.num_splits = a->num_splits;
+  c.chunk = a->split_chunk;
+  c.o_sb = a->o_stride_batch * ob;
+  c.o_st = a->o_stride_tok * ob;
+  c.o_sh = a->o_stride_head * ob;
+  c.lse_sb = a->lse_stride_batch;
+  c.lse_sh = a->lse_stride_head;
+  c.out_dtype = a->out_dtype;
+  if (launch_combine(c, (hipStream_t)stream) != hipSuccess) return FMHA_ERR_HIP;
+  return FMHA_OK;
+}
+
+int fmha_device_num_cus(int32_t* num_cus_out) {
+  if (!num_cus_out) return FMHA_ERR_INVALID_ARG;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FMHA_ERR_HIP;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return FMHA_ERR_HIP;
+  *num_cus_out = n;
+  return FMHA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Parameters handed from the host library to the kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+struct FwdParams {
+  const char* q;
+  const char* k;
+  const char* v;
+  char* o;
+  float* lse;        // may be null
+  float* o_part;     // split partials [S, total_q, Hq, Dv] (split mode)
+  float* lse_part;   // [S, Hq, total_q]
+  const int32_t* cu_q;  // null: fixed-length Q
+  const int32_t* cu_k;  // null: fixed-length K
+  const float* q_descale;  // fp8 only, may be null
+  const float* k_descale;
+  const float* v_descale;
+  int32_t batch;
+  int32_t seqlen_q;  // fixed-length Q
+  int32_t seqlen_k;  // fixed-length K
+  int32_t total_q;   // rows of the partial layout
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;     // hq / hkv
+  // strides in BYTES for q/k/v/o
+  int64_t q_sb, q_st, q_sh;
+  int64_t k_sb, k_st, k_sh;
+  int64_t v_sb, v_st, v_sh;
+  int64_t o_sb, o_st, o_sh;
+  // lse strides in elements
+  int64_t lse_sb, lse_sh;
+  float scale_log2;  // softmax scale * log2(e)
+  int32_t wl, wr;    // resolved window (-1 = unbounded), causal folded into wr
+  int32_t num_splits;  // 1: write final O/LSE; >1: write partials
+  int32_t chunk;       // keys per split
+  int32_t num_q_tiles;
+  int32_t out_dtype;
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  char* o;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t batch, seqlen_q, seqlen_k, max_seqlen_q, total_q;
+  int32_t hq, dv;
+  int32_t num_splits, chunk;
+  int64_t o_sb, o_st, o_sh;  // bytes
+  int64_t lse_sb, lse_sh;    // elements
+  int32_t out_dtype;
+};
+
+typedef hipError_t (*FwdLaunchFn)(const FwdParams&, int64_t grid, hipStream_t);
+
+// One compiled attention kernel instance.
+struct FwdKernel {
+  int dtype;
+  int dqk;
+  int dv;
+  int nwm;   // waves along query rows (16 rows each)
+  int nwk;   // waves splitting the key block
+  int bn;    // keys per wave per iteration
+  int id;
+  FwdLaunchFn launch;
+};
+
+// Registries, one per input dtype (defined in fmha_fwd_<dtype>.hip).
+const FwdKernel* registry_f32(int* n);
+const FwdKernel* registry_f16(int* n);
+const FwdKernel* registry_bf16(int* n);
+const FwdKernel* registry_fp8(int* n);
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+}  // namespace fmha

@@ -1,0 +1,346 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the CPU oracle,
+element by element, on seeded synthetic inputs of every workload shape.
+
+Tolerances are in tests/gpu_helpers.py.  Full-size prefill is checked on
+sampled rows the oracle computes one by one; everything else is checked on
+every output element.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fmha_synth as fs
+from fmha_synth import make_problem, raw_bits
+from gpu_helpers import (SENTINEL_LSE, SENTINEL_O, TOL_LSE, TOL_O, alloc_outputs,
+                         compare, out_dtype, run_gpu, run_oracle, to_packed, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module")
+def fmha():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import split_kv_flash_fmha_amd as m
+    return m
+
+
+def check(fmha, oracle, prob, splits=(0,), ref=None, label=""):
+    ref = ref or run_oracle(oracle, prob)
+    dev = upload(prob)
+    errs = {}
+    for s in splits:
+        announce(f"{prob.name} {label} splits={s} dtype={prob.dtype} lens_q={prob.lens_q[:8]} "
+                 f"lens_k={prob.lens_k[:8]} hq={prob.hq} hkv={prob.hkv} d={prob.dqk}/{prob.dv}")
+        out, lse = run_gpu(fmha, prob, num_kv_splits=s, dev=dev)
+        go, gl = to_packed(prob, out, lse)
+        errs[s] = compare(prob, go, gl, *ref, what=f"{prob.name} {label} splits={s}")
+    return errs
+
+
+# ---- tiny: fp32 and bf16, splits {1, 4} -----------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiny(fmha, oracle, dtype):
+    prob = fs.tiny(dtype)
+    check(fmha, oracle, prob, splits=(1, 4, 0))
+
+
+# ---- long-context decode: full size, split sweep ----------------------------
+
+def test_long_decode_split_sweep(fmha, oracle):
+    prob = fs.long_decode()
+    check(fmha, oracle, prob, splits=(0, 1, 2, 4, 8, 16, 32, 64, 128))
+
+
+# ---- GQA batched decode: varlen K, full size ------------------------------
+
+def test_gqa_decode(fmha, oracle):
+    prob = fs.gqa_decode()
+    check(fmha, oracle, prob, splits=(0, 1, 4))
+
+
+# ---- fp8 short cached-prefix prefill ---------------------------------------
+
+@pytest.mark.parametrize("seqlen_k", [11008, 16384])
+def test_fp8_prefix(fmha, oracle, seqlen_k):
+    prob = fs.fp8_prefix(seqlen_k)
+    check(fmha, oracle, prob, splits=(0, 1, 4, 8, 16))
+
+
+def test_fp8_prefix_causal_split(fmha, oracle):
+    # the combination the fp8 split-K page refuses (causal, Sq=70, Skv=16384,
+    # 4 splits) is computed exactly here: split == oracle
+    prob = fs.fp8_prefix(16384)
+    prob.causal = True
+    check(fmha, oracle, prob, splits=(4, 1, 0), label="causal")
+
+
+# ---- varlen prefill ------------------------------------------------------
+
+SMALL_SKEWED = [256, 32, 192, 64, 160, 96, 128, 96]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lengths", ["skewed", "equal"])
+def test_varlen_prefill_small(fmha, oracle, lengths, causal):
+    lens = SMALL_SKEWED if lengths == "skewed" else [128] * 8
+    prob = make_problem(f"varlen_small_{lengths}", dtype="f16", lens_q=lens, lens_k=lens,
+                        hq=16, hkv=16, dqk=128, dv=128, seed=4, varlen_q=True,
+                        varlen_k=True, causal=causal)
+    check(fmha, oracle, prob, splits=(0,))
+
+
+def sample_rows(prob, n_random=384, seed=0):
+    """Token/head pairs: first, last and tile-edge rows of every sequence + random."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    t0 = 0
+    for sq in prob.lens_q:
+        for i in (0, 1, 15, 16, 63, 64, 127, 128, sq // 2, sq - 2, sq - 1):
+            if 0 <= i < sq:
+                rows.add(t0 + i)
+        t0 += sq
+    tq = t0
+    rows |= set(int(x) for x in rng.integers(0, tq, size=n_random))
+    rows = sorted(rows)
+    rt = [t for t in rows for h in (0, prob.hq - 1)]
+    rh = [h for t in rows for h in (0, prob.hq - 1)]
+    return np.array(rt), np.array(rh)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lengths", ["skewed", "equal"])
+def test_varlen_prefill_full_sampled(fmha, oracle, lengths, causal):
+    prob = fs.varlen_prefill(lengths, causal)
+    announce(f"{prob.name} causal={causal} full size, sampled rows")
+    out, lse = run_gpu(fmha, prob)
+    go, gl = to_packed(prob, out, lse)
+    rt, rh = sample_rows(prob)
+    ro, rl = oracle.attention_rows(raw_bits(prob.q), raw_bits(prob.k), raw_bits(prob.v),
+                                   prob.dtype, rt, rh, cu_q=prob.cu_q, cu_k=prob.cu_k,
+                                   scale=1 / math.sqrt(prob.dqk), causal=causal)
+    err_o = float(np.max(np.abs(go[rt, rh] - ro)))
+    err_l = float(np.max(np.abs(gl[rh, rt] - rl)))
+    assert err_o <= TOL_O[prob.dtype], err_o
+    assert err_l <= TOL_LSE, err_l
+    # properties at every row: finite, |O| bounded by max |V| of the sequence
+    assert np.isfinite(go).all() and np.isfinite(gl).all()
+    assert np.abs(go).max() <= float(prob.v.abs().max()) + 1e-3
+
+
+# ---- edge set: lengths [1,0,63,64,65,128,129,700], GQA 8:2, bf16 ----------
+
+@pytest.mark.parametrize("mask", ["window", "none", "causal"])
+def test_edge_set(fmha, oracle, mask):
+    prob = fs.edge_set(causal=(mask == "causal"),
+                       window=(128, 0) if mask == "window" else (-1, -1))
+    check(fmha, oracle, prob, splits=(0, 1, 3), label=mask)
+
+
+@pytest.mark.parametrize("hkv", [8, 2, 1])
+@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+def test_edge_set_gqa_matrix(fmha, oracle, hkv, mask):
+    prob = make_problem("edge_gqa", dtype="bf16", lens_q=fs.EDGE_LENGTHS,
+                        lens_k=fs.EDGE_LENGTHS, hq=8, hkv=hkv, dqk=128, dv=128, seed=5,
+                        varlen_q=True, varlen_k=True, causal=(mask == "causal"),
+                        window=(128, 0) if mask == "window" else (-1, -1))
+    check(fmha, oracle, prob, splits=(0,), label=f"{mask} 8:{hkv}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_different_q_k_lengths(fmha, oracle, causal):
+    # q "3,(1,129,700),8,128"  k "3,(65,300,700),2,128"
+    prob = make_problem("qk_lengths", dtype="bf16", lens_q=[1, 129, 700],
+                        lens_k=[65, 300, 700], hq=8, hkv=2, dqk=128, dv=128, seed=6,
+                        varlen_q=True, varlen_k=True, causal=causal)
+    check(fmha, oracle, prob, splits=(0, 1, 2, 5), label=f"causal={causal}")
+
+
+@pytest.mark.parametrize("side", ["q", "k"])
+def test_varlen_one_side(fmha, oracle, side):
+    lens_q = [37, 37, 37] if side == "k" else [5, 90, 33]
+    lens_k = [200, 13, 77] if side == "k" else [150, 150, 150]
+    prob = make_problem(f"varlen_{side}_only", dtype="f16", lens_q=lens_q, lens_k=lens_k,
+                        hq=4, hkv=2, dqk=128, dv=128, seed=7, varlen_q=(side == "q"),
+                        varlen_k=(side == "k"), causal=True)
+    check(fmha, oracle, prob, splits=(0, 1, 3))
+
+
+@pytest.mark.parametrize("dtype,d,dv", [("bf16", 64, 64), ("bf16", 256, 256),
+                                        ("f16", 64, 64), ("f16", 256, 256),
+                                        ("f32", 128, 128), ("fp8_e4m3", 128, 128)])
+def test_head_dims(fmha, oracle, dtype, d, dv):
+    prob = make_problem(f"dims_{dtype}_{d}", dtype=dtype, lens_q=[1, 67, 130],
+                        lens_k=[300, 67, 513], hq=4, hkv=2, dqk=d, dv=dv, seed=8,
+                        varlen_q=True, varlen_k=True, causal=True)
+    check(fmha, oracle, prob, splits=(0, 1, 2))
+
+
+def test_queries_without_keys_complete(fmha):
+    # a sequence with queries but no keys: completes, rows untouched
+    prob = make_problem("no_keys", dtype="bf16", lens_q=[4, 9], lens_k=[0, 0], hq=2,
+                        hkv=2, dqk=64, dv=64, seed=9, varlen_q=True, varlen_k=True)
+    out, lse = run_gpu(fmha, prob, num_kv_splits=2)
+    assert (out.float() == SENTINEL_O).all() and (lse == SENTINEL_LSE).all()
+
+
+# ---- split partials and the combine --------------------------------------
+
+def test_partials_match_oracle_splits(fmha, oracle):
+    prob = make_problem("partials", dtype="bf16", lens_q=[1, 3, 2], lens_k=[700, 129, 0],
+                        hq=8, hkv=2, dqk=128, dv=128, seed=10, varlen_q=True,
+                        varlen_k=True, causal=True)
+    dev = upload(prob)
+    announce("partials vs oracle split partials")
+    o_part, lse_part, pl = fmha.splitkv_partials(
+        dev["q"], dev["k"], dev["v"], num_kv_splits=5, cu_seqlens_q=dev["cu_seqlens_q"],
+        cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+        max_seqlen_k=dev["max_seqlen_k"], causal=True)
+    torch.cuda.synchronize()
+    chunk = pl.split_chunk
+    assert pl.num_splits == 5 and chunk % pl.key_block == 0
+    scale = 1 / math.sqrt(128)
+    for s in range(5):
+        ro, rl = oracle.split_attention(raw_bits(prob.q), raw_bits(prob.k), raw_bits(prob.v),
+                                        "bf16", chunk=chunk, split=s, cu_q=prob.cu_q,
+                                        cu_k=prob.cu_k, scale=scale, causal=True)
+        go = o_part[s].double().cpu().numpy()
+        gl = lse_part[s].double().cpu().numpy()
+        t0 = 0
+        for sq, sk in zip(prob.lens_q, prob.lens_k):
+            if s < -(-sk // chunk):  # written splits only
+                sl = slice(t0, t0 + sq)
+                assert np.array_equal(np.isneginf(gl[:, sl]), np.isneginf(rl[:, sl]))
+                fin = ~np.isneginf(rl[:, sl])
+                assert np.abs(go[sl] - ro[sl]).max() <= TOL_O["bf16"]
+                if fin.any():
+                    assert np.abs(gl[:, sl][fin] - rl[:, sl][fin]).max() <= TOL_LSE
+            t0 += sq
+
+
+def test_combine_kernel_on_oracle_partials(fmha, oracle):
+    # partials computed by the oracle alone, rounded to fp32, combined on the GPU
+    prob = make_problem("combine", dtype="f32", lens_q=[2, 1, 3], lens_k=[90, 0, 33],
+                        hq=4, hkv=4, dqk=64, dv=64, seed=11, varlen_q=True, varlen_k=True,
+                        causal=True)
+    chunk, S = 16, 6
+    scale = 0.125
+    parts = [oracle.split_attention(raw_bits(prob.q), raw_bits(prob.k), raw_bits(prob.v),
+                                    "f32", chunk=chunk, split=s, cu_q=prob.cu_q,
+                                    cu_k=prob.cu_k, scale=scale, causal=True)
+             for s in range(S)]
+    o_part = np.stack([p[0] for p in parts]).astype(np.float32)
+    l_part = np.stack([p[1] for p in parts]).astype(np.float32)
+    ref_o, ref_l = oracle.combine(o_part.astype(np.float64), l_part.astype(np.float64),
+                                  chunk=chunk, cu_q=prob.cu_q, cu_k=prob.cu_k)
+    dev = upload(prob)
+    out, lse = alloc_outputs(prob, dev)
+    op = torch.from_numpy(np.nan_to_num(o_part, nan=0.0)).cuda()
+    lp = torch.from_numpy(np.nan_to_num(l_part, nan=-np.inf)).cuda()
+    announce("combine kernel on oracle partials")
+    fmha.splitkv_combine(op, lp, split_chunk=chunk, out=out, lse=lse,
+                         cu_seqlens_q=dev["cu_seqlens_q"], cu_seqlens_k=dev["cu_seqlens_k"],
+                         max_seqlen_q=dev["max_seqlen_q"])
+    torch.cuda.synchronize()
+    go, gl = to_packed(prob, out, lse)
+    compare(prob, go, gl, ref_o, ref_l, what="combine")
+    assert np.abs(go[~np.isnan(ref_o)] - ref_o[~np.isnan(ref_o)]).max() < 1e-5
+
+
+# ---- determinism, graph replay, guard bands, errors -------------------------
+
+def test_determinism(fmha):
+    prob = fs.edge_set()
+    dev = upload(prob)
+    announce("determinism")
+    a = run_gpu(fmha, prob, dev=dev, num_kv_splits=3)
+    b = run_gpu(fmha, prob, dev=dev, num_kv_splits=3)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+def test_graph_capture_replay(fmha):
+    prob = fs.fp8_prefix(11008)
+    dev = upload(prob)
+    out, lse = alloc_outputs(prob, dev)
+    kw = dict(cu_seqlens_q=None, cu_seqlens_k=None, num_kv_splits=8,
+              q_descale=dev["q_descale"], k_descale=dev["k_descale"],
+              v_descale=dev["v_descale"], out=out, lse=lse)
+    ws_args = fmha.make_args(dev["q"], dev["k"], dev["v"], num_kv_splits=8,
+                             num_cus=fmha.device_num_cus(), out=out, lse=lse)
+    ws = torch.empty(fmha.workspace_size(ws_args), dtype=torch.uint8, device="cuda")
+    announce("graph capture + replay")
+    fmha.fwd(dev["q"], dev["k"], dev["v"], workspace=ws, **kw)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    out.fill_(0)
+    lse.fill_(0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fmha.fwd(dev["q"], dev["k"], dev["v"], workspace=ws, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep} O"
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep} LSE"
+        _ = (dev["q"].float().sum() + 1).item()  # unrelated eager work between replays
+
+
+def test_guard_bands(fmha):
+    prob = make_problem("guards", dtype="bf16", lens_q=[3, 65, 1], lens_k=[129, 65, 40],
+                        hq=8, hkv=2, dqk=128, dv=128, seed=12, varlen_q=True, varlen_k=True,
+                        causal=True)
+    dev = upload(prob)
+    tq = sum(prob.lens_q)
+    pad = 4096
+    ob = torch.full((pad + tq * 8 * 128 + pad,), SENTINEL_O, dtype=torch.bfloat16, device="cuda")
+    lb = torch.full((pad + 8 * tq + pad,), SENTINEL_LSE, dtype=torch.float32, device="cuda")
+    out = ob[pad:pad + tq * 8 * 128].view(tq, 8, 128)
+    lse = lb[pad:pad + 8 * tq].view(8, tq)
+    for s in (1, 4):
+        announce(f"guard bands splits={s}")
+        run_gpu(fmha, prob, dev=dev, out=out, lse=lse, num_kv_splits=s)
+        assert (ob[:pad].float() == SENTINEL_O).all() and (ob[-pad:].float() == SENTINEL_O).all()
+        assert (lb[:pad] == SENTINEL_LSE).all() and (lb[-pad:] == SENTINEL_LSE).all()
+
+
+def test_errors_write_nothing(fmha):
+    prob = fs.tiny("bf16")
+    dev = upload(prob)
+    out, lse = alloc_outputs(prob, dev)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    bad = [
+        dict(softmax_scale=-1.0),
+        dict(window=(-2, 0)),
+        dict(num_kv_splits=257),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            fmha.fwd(q, k, v, out=out, lse=lse, **kw)
+    with pytest.raises(ValueError):  # Hq % Hkv != 0
+        fmha.fwd(q[:, :, :3], k, v, out=out[:, :, :3], lse=lse[:, :3])
+    with pytest.raises(ValueError):  # no kernel for head dim 48
+        fmha.fwd(q[..., :48], k[..., :48], v, out=out, lse=lse)
+    with pytest.raises(ValueError):  # workspace too small
+        fmha.fwd(q, k, v, out=out, lse=lse, num_kv_splits=4,
+                 workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert (out.float() == SENTINEL_O).all() and (lse == SENTINEL_LSE).all()

@@ -1,0 +1,245 @@
+"""CPU-only tests of the C ABI's host logic: the library loads, exports every
+symbol include/fmha.h declares, and validates / resolves arguments (default
+scale, windows, split count, workspace size, error codes) without a GPU.
+No compute call is made here.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import split_kv_flash_fmha_amd as fmha
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x7F0000000000  # 16-byte aligned stand-in device address (never dereferenced)
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fmha.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fmha_\w+)\s*\(", src, re.M)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 8, names
+    for n in names:
+        assert hasattr(fmha.lib, n), f"{n} declared in include/fmha.h but not exported"
+
+
+def make(*, dtype=2, out_dtype=None, batch=1, sq=1, sk=1024, hq=4, hkv=4, dqk=64, dv=64,
+         varlen_q=False, varlen_k=False, max_q=None, max_k=None, total_q=None, total_k=None,
+         scale=0.0, causal=False, window=(-1, -1), splits=1, num_cus=256, lse=True,
+         workspace=None, workspace_bytes=0):
+    a = fmha.FwdArgs()
+    a.q = a.k = a.v = a.out = FAKE
+    a.lse = FAKE if lse else None
+    a.batch = batch
+    if varlen_q:
+        a.cu_seqlens_q = FAKE
+        a.total_q = total_q if total_q is not None else batch * sq
+        a.max_seqlen_q = max_q if max_q is not None else sq
+    else:
+        a.seqlen_q = sq
+    if varlen_k:
+        a.cu_seqlens_k = FAKE
+        a.total_k = total_k if total_k is not None else batch * sk
+        a.max_seqlen_k = max_k if max_k is not None else sk
+    else:
+        a.seqlen_k = sk
+    a.num_heads_q, a.num_heads_kv, a.head_dim_qk, a.head_dim_v = hq, hkv, dqk, dv
+    a.q_stride_head, a.q_stride_tok, a.q_stride_batch = dqk, hq * dqk, sq * hq * dqk
+    a.k_stride_head, a.k_stride_tok, a.k_stride_batch = dqk, hkv * dqk, sk * hkv * dqk
+    a.v_stride_head, a.v_stride_tok, a.v_stride_batch = dv, hkv * dv, sk * hkv * dv
+    a.o_stride_head, a.o_stride_tok, a.o_stride_batch = dv, hq * dv, sq * hq * dv
+    a.lse_stride_head, a.lse_stride_batch = sq, hq * sq
+    a.in_dtype = dtype
+    a.out_dtype = out_dtype if out_dtype is not None else (2 if dtype == 3 else dtype)
+    a.softmax_scale = scale
+    a.causal = int(causal)
+    a.window_left, a.window_right = window
+    a.num_kv_splits = splits
+    a.num_cus = num_cus
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace, workspace_bytes
+    return a
+
+
+def check(a):
+    p = fmha.Plan()
+    st = fmha.lib.fmha_fwd_check(ctypes.byref(a), ctypes.byref(p))
+    return st, p
+
+
+# ---- default softmax scale (pinned for non-square shapes) ---------------------
+
+@pytest.mark.parametrize("varlen,sq,d", [(True, 129, 64), (False, 700, 64), (True, 129, 128),
+                                         (False, 129, 128)])
+def test_default_scale_uses_head_dim(varlen, sq, d):
+    a = make(varlen_q=varlen, sq=sq, dqk=d, dv=d, sk=sq, varlen_k=varlen, splits=1)
+    st, p = check(a)
+    assert st == OK
+    assert p.softmax_scale == np.float32(1.0 / math.sqrt(d))
+    assert p.softmax_scale != np.float32(1.0 / math.sqrt(sq))
+
+
+def test_explicit_scale_passes_through():
+    st, p = check(make(scale=0.3))
+    assert st == OK and p.softmax_scale == np.float32(0.3)
+
+
+def test_fp8_default_scale_is_qk_head_dim():
+    st, p = check(make(dtype=3, dqk=192, dv=128, sq=70, sk=16384, hq=12, hkv=12))
+    assert st == OK and p.softmax_scale == np.float32(1 / math.sqrt(192))
+
+
+# ---- masks --------------------------------------------------------------------
+
+@pytest.mark.parametrize("window,causal,expect", [((-1, -1), True, (-1, 0)), ((128, 0), False, (128, 0)),
+                                                  ((5, 7), True, (5, 0)), ((3, -1), False, (3, -1))])
+def test_window_resolution(window, causal, expect):
+    st, p = check(make(window=window, causal=causal, sq=64, sk=64))
+    assert st == OK and (p.window_left, p.window_right) == expect
+
+
+# ---- errors -------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(hq=0), INVALID),
+    (dict(window=(-2, 0)), INVALID),
+    (dict(window=(0, -5)), INVALID),
+    (dict(scale=-0.5), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(splits=-1), INVALID),
+    (dict(splits=257), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(dqk=48, dv=48), UNSUPPORTED),
+    (dict(dqk=128, dv=64), UNSUPPORTED),
+    (dict(dtype=2, out_dtype=1), UNSUPPORTED),
+    (dict(dtype=3, out_dtype=3), INVALID),
+    (dict(dtype=3, out_dtype=1, dqk=128, dv=128), UNSUPPORTED),
+    (dict(varlen_q=True, max_q=10, total_q=5), INVALID),
+    (dict(sq=-1), INVALID),
+    (dict(splits=4), WORKSPACE),
+])
+def test_rejections(kw, code):
+    st, _ = check(make(**kw))
+    assert st == code, (kw, st)
+
+
+def test_misaligned_pointer_and_stride():
+    a = make()
+    a.q = FAKE + 2
+    assert check(a)[0] == INVALID
+    a = make()
+    a.k_stride_tok = 4 * 64 + 1  # not a multiple of 16 bytes
+    assert check(a)[0] == INVALID
+
+
+def test_null_pointers_rejected_unless_empty():
+    a = make()
+    a.out = None
+    assert check(a)[0] == INVALID
+    a = make(batch=0)
+    a.out = a.q = a.k = a.v = None
+    assert check(a)[0] == OK
+
+
+def test_status_strings():
+    for s in range(5):
+        assert fmha.lib.fmha_status_str(s)
+    assert b"unknown" in fmha.lib.fmha_status_str(99)
+
+
+# ---- splits and workspace -------------------------------------------------------
+
+def test_explicit_splits_and_workspace_size():
+    a = make(sk=1024, splits=4, hq=4, hkv=4, dv=64)
+    n = ctypes.c_int32()
+    assert fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n)) == OK and n.value == 4
+    sz = ctypes.c_size_t()
+    assert fmha.lib.fmha_fwd_workspace_size(ctypes.byref(a), ctypes.byref(sz)) == OK
+    tq, hq, dv, S = 1, 4, 64, 4
+    al = lambda x: (x + 255) // 256 * 256
+    assert sz.value == al(S * tq * hq * dv * 4) + al(S * hq * tq * 4)
+    a.workspace, a.workspace_bytes = FAKE, sz.value
+    st, p = check(a)
+    assert st == OK and p.num_splits == 4 and p.split_chunk * 4 >= 1024
+    assert p.split_chunk % p.key_block == 0
+    assert p.lse_part_offset >= S * tq * hq * dv * 4 and p.lse_part_offset % 256 == 0
+    a.workspace_bytes = sz.value - 1
+    assert check(a)[0] == WORKSPACE
+    a.workspace_bytes = sz.value
+    a.workspace = FAKE + 16  # not 256-byte aligned
+    assert check(a)[0] == WORKSPACE
+
+
+def test_many_splits_beyond_key_blocks_are_honoured():
+    a = make(sk=100, splits=64)
+    n = ctypes.c_int32()
+    assert fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n)) == OK
+    assert n.value == 64
+
+
+def test_auto_splits_long_decode_fills_device():
+    a = make(sq=1, sk=131072, hq=32, hkv=32, dqk=128, dv=128, splits=0)
+    n = ctypes.c_int32()
+    assert fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n)) == OK
+    assert 8 <= n.value <= 128
+    # units x splits cover the device several times over
+    assert n.value * 32 >= 2 * 256
+
+
+def test_auto_splits_scale_with_cu_count():
+    base = dict(sq=1, sk=131072, hq=32, hkv=32, dqk=128, dv=128)
+    s = []
+    for cus in (64, 256):
+        a = make(num_cus=cus, splits=0, **base)
+        n = ctypes.c_int32()
+        fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n))
+        s.append(n.value)
+    assert s[0] < s[1]
+
+
+def test_auto_splits_off_for_prefill():
+    a = make(varlen_q=True, varlen_k=True, batch=8, sq=2048, sk=2048, hq=16, hkv=16, dqk=128,
+             dv=128, dtype=1, max_q=4096, max_k=4096, total_q=16384, total_k=16384, splits=0)
+    n = ctypes.c_int32()
+    assert fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n)) == OK and n.value == 1
+
+
+def test_auto_splits_short_prefix_fp8():
+    a = make(dtype=3, sq=70, sk=16384, hq=12, hkv=12, dqk=192, dv=128, splits=0)
+    n = ctypes.c_int32()
+    assert fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n)) == OK
+    assert n.value > 1
+
+
+def test_gqa_rows_packed_into_one_tile():
+    # 4 query heads per kv head, one query token: a single 16-row tile
+    st, p = check(make(sq=1, sk=4096, hq=32, hkv=8, dqk=128, dv=128, splits=1))
+    assert st == OK and p.num_q_tiles == 1 and p.rows_per_tile == 16
+    assert p.grid_main == 8  # batch 1 x 8 kv heads x 1 tile x 1 split
+
+
+def test_combine_rejections():
+    c = fmha.CombineArgs()
+    c.o_part = c.lse_part = c.out = FAKE
+    c.batch, c.seqlen_q, c.seqlen_k = 1, 1, 64
+    c.num_heads_q, c.head_dim_v, c.num_splits, c.split_chunk = 4, 64, 2, 32
+    c.o_stride_head, c.o_stride_tok, c.o_stride_batch = 64, 256, 256
+    c.out_dtype = 2
+    c.num_splits = 0
+    assert fmha.lib.fmha_splitkv_combine(ctypes.byref(c), None) == INVALID
+    c.num_splits, c.split_chunk = 2, 0
+    assert fmha.lib.fmha_splitkv_combine(ctypes.byref(c), None) == INVALID
+    c.split_chunk, c.out_dtype = 32, 3
+    assert fmha.lib.fmha_splitkv_combine(ctypes.byref(c), None) == INVALID
