@@ -196,17 +196,21 @@ typedef struct fmha_fwd_plan {
 } fmha_fwd_plan;
 
 /*
- * Validate `args` and resolve defaults, split count and workspace size.
- * Host only: makes no HIP call and reads no device memory, so it runs without
- * a GPU.  `plan` may be NULL.  The workspace pointer/size are checked only
- * when a split is used.  Returns FMHA_OK or an error code.
+ * Validate `args` for an fmha_fwd call and resolve defaults, split count and
+ * workspace size.  Host only: makes no HIP call and reads no device memory, so
+ * it runs without a GPU.  `plan` may be NULL.  The workspace pointer/size are
+ * checked only when a split is used.  With args->out == NULL the arguments are
+ * checked for fmha_fwd_splitkv_partials instead.  Returns FMHA_OK or an error
+ * code.
  */
 int fmha_fwd_check(const fmha_fwd_args* args, fmha_fwd_plan* plan);
 
-/* Resolved split count for `args` (host only; automatic when num_kv_splits == 0). */
+/* Resolved split count for `args` (host only; automatic when num_kv_splits == 0).
+ * A shape query: data pointers are not checked and may be NULL. */
 int fmha_num_splits(const fmha_fwd_args* args, int32_t* splits_out);
 
-/* Workspace bytes `args` needs (host only; 0 when no split is used). */
+/* Workspace bytes `args` needs (host only; 0 when no split is used).  A shape
+ * query: data pointers are not checked and may be NULL. */
 int fmha_fwd_workspace_size(const fmha_fwd_args* args, size_t* bytes_out);
 
 /*
@@ -221,7 +225,7 @@ int fmha_fwd(const fmha_fwd_args* args, void* stream);
  * split with no allowed key) into the workspace at the plan's offsets, for
  * every split s < ceil(sk_b / chunk) of every sequence b with keys.  Requires
  * a resolved split count > 1 (else FMHA_ERR_INVALID_ARG).  `out`/`lse` are
- * not touched.  fmha_fwd is this call followed by fmha_splitkv_combine.
+ * not touched and may be NULL.  fmha_fwd is this call followed by fmha_splitkv_combine.
  */
 int fmha_fwd_splitkv_partials(const fmha_fwd_args* args, void* stream);
 

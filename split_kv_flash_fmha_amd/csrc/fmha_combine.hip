@@ -4,9 +4,12 @@
 // combine): for row (t, h) with partials (O_s, lse_s), s < S_b,
 //   L = max_s lse_s;  L = -inf -> O = 0, LSE = -inf;
 //   LSE = L + ln sum_s exp(lse_s - L);  O = sum_s exp(lse_s - LSE) O_s.
-// One wavefront per (query row, head); lanes run along Dv so partial rows
-// are read with contiguous 8-byte loads.  Memory-bound and small next to the
-// attention launch.
+//
+// One 256-thread workgroup per (query row, head).  Thread s < S_b loads
+// lse_s, the workgroup reduces max and sum, and each split's weight is
+// computed once into LDS.  The Dv/4 16-byte column chunks x (256 / (Dv/4))
+// split groups then read disjoint partial rows in parallel (no serial chain
+// of dependent loads) and the split groups are summed through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,8 +19,21 @@ namespace fmha {
 
 namespace {
 
+constexpr int kThreads = 256;
 constexpr float kLog2eC = 1.4426950408889634f;
 constexpr float kLn2C = 0.6931471805599453f;
+
+typedef float f32x4c __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2c __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack2(float a, float b, int out_dtype) {
+  if (out_dtype == DT_BF16) {
+    __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  }
+  _Float16 x = static_cast<_Float16>(a), y = static_cast<_Float16>(b);
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -30,25 +46,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b, int out_dtype) {
-  if (out_dtype == DT_BF16) {
-    __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-  }
-  _Float16 x = static_cast<_Float16>(a), y = static_cast<_Float16>(b);
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
+__global__ __launch_bounds__(kThreads) void fmha_combine_kernel(CombineParams p) {
+  __shared__ float w_s[kThreads];
+  __shared__ float red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) f32x4c part[kThreads];
 
-constexpr int kWaves = 4;
-
-__global__ __launch_bounds__(64 * kWaves) void fmha_combine_kernel(CombineParams p) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t per_b = ((int64_t)p.max_seqlen_q * p.hq + kWaves - 1) / kWaves;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t per_b = (int64_t)p.max_seqlen_q * p.hq;
   const int b = (int)(blockIdx.x / per_b);
-  const int64_t item = (int64_t)(blockIdx.x % per_b) * kWaves + wave;
-  const int h = (int)(item % p.hq);
-  const int i = (int)(item / p.hq);
+  const int64_t rem = blockIdx.x % per_b;
+  const int i = (int)(rem / p.hq);
+  const int h = (int)(rem % p.hq);
 
   int q_off, sq, sk;
   if (p.cu_q) {
@@ -59,45 +68,54 @@ __global__ __launch_bounds__(64 * kWaves) void fmha_combine_kernel(CombineParams
     sq = p.seqlen_q;
   }
   sk = p.cu_k ? p.cu_k[b + 1] - p.cu_k[b] : p.seqlen_k;
-  if (i >= sq || sk <= 0) return;  // rows of sequences without keys: untouched
+  if (i >= sq || sk <= 0) return;  // rows of sequences without keys: untouched (uniform)
   const int nsb = min((sk + p.chunk - 1) / p.chunk, p.num_splits);
   const int64_t t = (int64_t)q_off + i;
-  const float* lp = p.lse_part + (int64_t)h * p.total_q + t;
   const int64_t lse_split_stride = (int64_t)p.hq * p.total_q;
 
-  float L = -INFINITY;
-  for (int s = lane; s < nsb; s += 64) L = fmaxf(L, lp[s * lse_split_stride]);
-  L = wave_max(L);
+  // split weights: w_s = exp(lse_s - LSE)
+  const float my_lse = tid < nsb ? p.lse_part[(int64_t)tid * lse_split_stride + (int64_t)h * p.total_q + t]
+                                 : -INFINITY;
+  float v = wave_max(my_lse);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float L = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float e = (L != -INFINITY && tid < nsb) ? exp2f((my_lse - L) * kLog2eC) : 0.f;
+  e = wave_sum(e);
+  if (lane == 0) red[wave] = e;
+  __syncthreads();
+  const float sum = red[0] + red[1] + red[2] + red[3];
+  const float total = L == -INFINITY ? -INFINITY : L + log2f(sum) * kLn2C;
+  w_s[tid] = (tid < nsb && total != -INFINITY) ? exp2f((my_lse - total) * kLog2eC) : 0.f;
+  __syncthreads();
 
-  float total = -INFINITY;
-  if (L != -INFINITY) {
-    float sum = 0.f;
-    for (int s = lane; s < nsb; s += 64) sum += exp2f((lp[s * lse_split_stride] - L) * kLog2eC);
-    sum = wave_sum(sum);
-    total = L + log2f(sum) * kLn2C;
+  // weighted sum: thread = (split group sg, 4-column chunk c)
+  const int nchunk = p.dv >> 2;
+  const int ngroups = kThreads / nchunk;
+  const int c = tid % nchunk, sg = tid / nchunk;
+  f32x4c acc = {0.f, 0.f, 0.f, 0.f};
+  if (sg < ngroups) {
+    const int64_t o_split_stride = (int64_t)p.total_q * p.hq * p.dv;
+    const float* op = p.o_part + (t * p.hq + h) * p.dv + 4 * c;
+#pragma unroll 4
+    for (int s = sg; s < nsb; s += ngroups) acc += w_s[s] * *(const f32x4c*)(op + s * o_split_stride);
   }
-
-  char* orow = p.o + (p.cu_q ? (int64_t)(q_off + i) * p.o_st : (int64_t)b * p.o_sb + (int64_t)i * p.o_st) +
-               (int64_t)h * p.o_sh;
-  const int64_t o_split_stride = (int64_t)p.total_q * p.hq * p.dv;
-  const float* op = p.o_part + (t * p.hq + h) * p.dv;
-  for (int d = lane * 2; d < p.dv; d += 128) {
-    float a0 = 0.f, a1 = 0.f;
-    if (total != -INFINITY) {
-      for (int s = 0; s < nsb; ++s) {
-        const float w = exp2f((lp[s * lse_split_stride] - total) * kLog2eC);
-        const float2 v = *(const float2*)(op + s * o_split_stride + d);
-        a0 += w * v.x;
-        a1 += w * v.y;
-      }
-    }
+  part[tid] = acc;
+  __syncthreads();
+  if (tid < nchunk) {
+    f32x4c o = part[tid];
+    for (int g = 1; g < ngroups; ++g) o += part[g * nchunk + tid];
+    char* orow = p.o + (p.cu_q ? (int64_t)(q_off + i) * p.o_st : (int64_t)b * p.o_sb + (int64_t)i * p.o_st) +
+                 (int64_t)h * p.o_sh;
     if (p.out_dtype == DT_F32) {
-      *(float2*)(orow + (int64_t)d * 4) = make_float2(a0, a1);
+      *(f32x4c*)(orow + (int64_t)tid * 16) = o;
     } else {
-      *(uint32_t*)(orow + (int64_t)d * 2) = pack2(a0, a1, p.out_dtype);
+      u32x2c wv = {pack2(o.x, o.y, p.out_dtype), pack2(o.z, o.w, p.out_dtype)};
+      *(u32x2c*)(orow + (int64_t)tid * 8) = wv;
     }
   }
-  if (p.lse && lane == 0) {
+  if (p.lse && tid == 0) {
     const int64_t li = p.cu_q ? (int64_t)h * p.lse_sh + q_off + i : (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i;
     p.lse[li] = total;
   }
@@ -106,10 +124,9 @@ __global__ __launch_bounds__(64 * kWaves) void fmha_combine_kernel(CombineParams
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  const int64_t items = (int64_t)p.max_seqlen_q * p.hq;
-  const int64_t gx = (items + kWaves - 1) / kWaves;
-  if (gx <= 0 || p.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fmha_combine_kernel, dim3((uint32_t)(gx * p.batch)), dim3(64 * kWaves), 0, stream, p);
+  const int64_t items = (int64_t)p.max_seqlen_q * p.hq * p.batch;
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fmha_combine_kernel, dim3((uint32_t)items), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -25,4 +25,10 @@ const FwdKernel* registry_f32(int* n) {
   return kTable;
 }
 
+// No decode instances for fp32 inputs (the LDS transpose reads are 8/16-bit).
+const FwdKernel* registry_f32_decode(int* n) {
+  *n = 0;
+  return nullptr;
+}
+
 }  // namespace fmha

@@ -1,5 +1,6 @@
 // Compiled attention kernel instances for fp8 inputs (generated list;
 // edit here and in the host's selection rules together).
+#include "fmha_decode_kernel.h"
 #include "fmha_fwd_kernel.h"
 
 namespace fmha {
@@ -23,6 +24,20 @@ static const FwdKernel kTable[] = {
 const FwdKernel* registry_fp8(int* n) {
   *n = (int)(sizeof(kTable) / sizeof(kTable[0]));
   return kTable;
+}
+
+// Decode instances (<= 16 query rows per (sequence, kv head)): bn = 0 marks them.
+#define FMHA_DEC(DQK, DV, NW, ID) \
+  {DT_FP8, DQK, DV, 1, NW, 0, ID, &launch_decode<DecCfg<DT_FP8, DQK, DV, NW>>}
+
+static const FwdKernel kDecTable[] = {
+    FMHA_DEC(128, 128, 4, 100),
+    FMHA_DEC(192, 128, 4, 101),
+};
+
+const FwdKernel* registry_fp8_decode(int* n) {
+  *n = (int)(sizeof(kDecTable) / sizeof(kDecTable[0]));
+  return kDecTable;
 }
 
 }  // namespace fmha

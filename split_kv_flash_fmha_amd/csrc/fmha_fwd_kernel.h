@@ -70,14 +70,12 @@ struct Elem<DT_FP8> {
 template <int DT>
 __device__ __forceinline__ f32x4 mfma_chunk(f32x4 acc, u32x4 a, u32x4 b) {
   if constexpr (DT == DT_F32) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x),
-                                               __builtin_bit_cast(float, b.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.y),
-                                               __builtin_bit_cast(float, b.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.z),
-                                               __builtin_bit_cast(float, b.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.w),
-                                               __builtin_bit_cast(float, b.w), acc, 0, 0, 0);
+    // one fp32 contraction slot per lane per instruction; components are
+    // converted by value (bit-casting a vector component reads element 0)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
   } else if constexpr (DT == DT_F16) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
@@ -114,10 +112,10 @@ template <int DT>
 __device__ __forceinline__ u32x4 pack_p(const f32x4* p) {
   u32x4 r;
   if constexpr (DT == DT_F32) {
-    r.x = __builtin_bit_cast(uint32_t, p[0].x);
-    r.y = __builtin_bit_cast(uint32_t, p[0].y);
-    r.z = __builtin_bit_cast(uint32_t, p[0].z);
-    r.w = __builtin_bit_cast(uint32_t, p[0].w);
+    r.x = __float_as_uint(p[0].x);
+    r.y = __float_as_uint(p[0].y);
+    r.z = __float_as_uint(p[0].z);
+    r.w = __float_as_uint(p[0].w);
   } else if constexpr (DT == DT_F16) {
     r.x = pack_f16x2(p[0].x, p[0].y);
     r.y = pack_f16x2(p[0].z, p[0].w);

@@ -58,6 +58,24 @@ void pick_shape(int64_t rows, int* nwm, int* nwk) {
   }
 }
 
+const FwdKernel* decode_registry(int dt, int* n) {
+  switch (dt) {
+    case FMHA_DTYPE_F32: return registry_f32_decode(n);
+    case FMHA_DTYPE_F16: return registry_f16_decode(n);
+    case FMHA_DTYPE_BF16: return registry_bf16_decode(n);
+    case FMHA_DTYPE_FP8_E4M3: return registry_fp8_decode(n);
+    default: *n = 0; return nullptr;
+  }
+}
+
+const FwdKernel* find_decode(int dt, int dqk, int dv) {
+  int n = 0;
+  const FwdKernel* t = decode_registry(dt, &n);
+  for (int i = 0; i < n; ++i)
+    if (t[i].dqk == dqk && t[i].dv == dv) return &t[i];
+  return nullptr;
+}
+
 const FwdKernel* find_exact(int dt, int dqk, int dv, int nwm, int nwk) {
   int n = 0;
   const FwdKernel* t = registry(dt, &n);
@@ -92,11 +110,13 @@ struct Resolved {
 // Automatic split count.  Parallel units of the non-split grid are
 // (sequence, kv head, query tile); when they cannot fill the device the key
 // range is cut so that about kTargetPerCu workgroups per compute unit exist,
-// each streaming at least kMinChunk keys (the split sweeps on the pages show
+// each streaming at least kMinChunk keys.  The split sweeps on the pages show
 // time falling steeply until the grid covers the machine and flattening or
-// rising a little past that point).
+// rising a little past that point; on MI355X the decode kernel (2 resident
+// workgroups per CU) keeps improving until each CU has seen ~8 waves of
+// workgroups, which also evens out sequences of different lengths.
 int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num_cus) {
-  constexpr int kTargetPerCu = 4;
+  constexpr int kTargetPerCu = 16;
   constexpr int64_t kMinChunk = 256;
   if (sk_max <= 0) return 1;
   const int64_t target = (int64_t)kTargetPerCu * num_cus;
@@ -110,7 +130,12 @@ int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num
   return (int)s;
 }
 
-int resolve(const fmha_fwd_args* a, bool check_ws, Resolved* r) {
+// What a caller is about to do with the arguments: a pure shape query checks
+// no pointer, the partials launch needs q/k/v and the workspace, the full
+// forward also needs out.
+enum Mode { kQuery, kPartials, kFull };
+
+int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   if (!a || !r) return FMHA_ERR_INVALID_ARG;
   memset(r, 0, sizeof(*r));
   const int eb = elem_bytes(a->in_dtype);
@@ -157,18 +182,22 @@ int resolve(const fmha_fwd_args* a, bool check_ws, Resolved* r) {
   const int G = a->num_heads_q / a->num_heads_kv;
   int nwm = 1, nwk = 4;
   pick_shape(r->sq_max * G, &nwm, &nwk);
-  const FwdKernel* kern = find_kernel(a->in_dtype, a->head_dim_qk, a->head_dim_v, nwm, nwk);
+  const FwdKernel* kern = nullptr;
+  if (r->sq_max * G <= 16) kern = find_decode(a->in_dtype, a->head_dim_qk, a->head_dim_v);
+  if (!kern) kern = find_kernel(a->in_dtype, a->head_dim_qk, a->head_dim_v, nwm, nwk);
   if (!kern) return FMHA_ERR_UNSUPPORTED;
   r->kernel = kern;
   pl.kernel_id = a->in_dtype * 1000 + kern->id;
   pl.rows_per_tile = 16 * kern->nwm;
-  pl.key_block = kern->nwk * kern->bn;
+  // decode kernels stream 32-key blocks per wave; splits are cut in multiples of that
+  pl.key_block = kern->bn > 0 ? kern->nwk * kern->bn : 32;
   const int64_t rows = r->sq_max * G;
   pl.num_q_tiles = (int32_t)((rows + pl.rows_per_tile - 1) / pl.rows_per_tile);
 
-  r->empty = a->batch == 0 || r->total_q == 0 || r->sq_max == 0;
-  if (!r->empty) {
-    if (!a->q || !a->k || !a->v || !a->out) return FMHA_ERR_INVALID_ARG;
+  // nothing to compute (and nothing written): no query rows, or no key anywhere
+  r->empty = a->batch == 0 || r->total_q == 0 || r->sq_max == 0 || r->total_k == 0 || r->sk_max == 0;
+  if (!r->empty && mode != kQuery) {
+    if (!a->q || !a->k || !a->v || (mode == kFull && !a->out)) return FMHA_ERR_INVALID_ARG;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->out, 16))
       return FMHA_ERR_INVALID_ARG;
     if (a->lse && !aligned(a->lse, 4)) return FMHA_ERR_INVALID_ARG;
@@ -210,9 +239,9 @@ int resolve(const fmha_fwd_args* a, bool check_ws, Resolved* r) {
   }
   pl.grid_main = r->empty ? 0 : (int64_t)S * units;
   if (pl.grid_main >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
-  pl.grid_combine = (r->empty || S == 1) ? 0 : ((r->sq_max * a->num_heads_q + 3) / 4) * a->batch;
+  pl.grid_combine = (r->empty || S == 1) ? 0 : r->sq_max * a->num_heads_q * a->batch;
   if (pl.grid_combine >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
-  if (check_ws && S > 1 && !r->empty) {
+  if (mode != kQuery && S > 1 && !r->empty) {
     if (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < pl.workspace_bytes)
       return FMHA_ERR_WORKSPACE;
   }
@@ -318,7 +347,8 @@ const char* fmha_status_str(int status) {
 
 int fmha_fwd_check(const fmha_fwd_args* args, fmha_fwd_plan* plan) {
   Resolved r;
-  const int st = resolve(args, true, &r);
+  // with out == NULL the arguments are checked for a partials-only launch
+  const int st = resolve(args, (args && args->out) ? kFull : kPartials, &r);
   if (st == FMHA_OK && plan) *plan = r.plan;
   return st;
 }
@@ -326,7 +356,7 @@ int fmha_fwd_check(const fmha_fwd_args* args, fmha_fwd_plan* plan) {
 int fmha_num_splits(const fmha_fwd_args* args, int32_t* splits_out) {
   if (!splits_out) return FMHA_ERR_INVALID_ARG;
   Resolved r;
-  const int st = resolve(args, false, &r);
+  const int st = resolve(args, kQuery, &r);
   if (st == FMHA_OK) *splits_out = r.plan.num_splits;
   return st;
 }
@@ -334,14 +364,14 @@ int fmha_num_splits(const fmha_fwd_args* args, int32_t* splits_out) {
 int fmha_fwd_workspace_size(const fmha_fwd_args* args, size_t* bytes_out) {
   if (!bytes_out) return FMHA_ERR_INVALID_ARG;
   Resolved r;
-  const int st = resolve(args, false, &r);
+  const int st = resolve(args, kQuery, &r);
   if (st == FMHA_OK) *bytes_out = r.plan.workspace_bytes;
   return st;
 }
 
 int fmha_fwd(const fmha_fwd_args* args, void* stream) {
   Resolved r;
-  int st = resolve(args, true, &r);
+  int st = resolve(args, kFull, &r);
   if (st != FMHA_OK) return st;
   if (r.empty || r.plan.grid_main == 0) return FMHA_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -356,7 +386,7 @@ int fmha_fwd(const fmha_fwd_args* args, void* stream) {
 
 int fmha_fwd_splitkv_partials(const fmha_fwd_args* args, void* stream) {
   Resolved r;
-  int st = resolve(args, true, &r);
+  int st = resolve(args, kPartials, &r);
   if (st != FMHA_OK) return st;
   if (r.plan.num_splits <= 1) return FMHA_ERR_INVALID_ARG;
   if (r.empty || r.plan.grid_main == 0) return FMHA_OK;
@@ -369,7 +399,10 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
   if (!a) return FMHA_ERR_INVALID_ARG;
   const int ob = elem_bytes(a->out_dtype);
   if (ob == 0 || a->out_dtype == FMHA_DTYPE_FP8_E4M3) return FMHA_ERR_INVALID_ARG;
-  if (a->batch < 0 || a->num_heads_q <= 0 || a->head_dim_v <= 0 || a->head_dim_v % 2) return FMHA_ERR_INVALID_ARG;
+  // the combine moves 4 consecutive Dv elements per thread, one workgroup per row
+  if (a->batch < 0 || a->num_heads_q <= 0 || a->head_dim_v <= 0 || a->head_dim_v % 4 ||
+      a->head_dim_v > 1024)
+    return FMHA_ERR_INVALID_ARG;
   if (a->num_splits < 1 || a->num_splits > FMHA_MAX_SPLITS || a->split_chunk < 1) return FMHA_ERR_INVALID_ARG;
   const bool vq = a->cu_seqlens_q != nullptr;
   const int64_t sq_max = vq ? a->max_seqlen_q : a->seqlen_q;
@@ -378,12 +411,12 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
   if (vq && a->max_seqlen_q > a->total_q) return FMHA_ERR_INVALID_ARG;
   if (a->batch == 0 || total_q == 0 || sq_max == 0) return FMHA_OK;
   if (!a->o_part || !a->lse_part || !a->out) return FMHA_ERR_INVALID_ARG;
-  if (!aligned(a->o_part, 8) || !aligned(a->lse_part, 4) || !aligned(a->out, 2 * ob)) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(a->o_part, 16) || !aligned(a->lse_part, 4) || !aligned(a->out, 4 * ob)) return FMHA_ERR_INVALID_ARG;
   if (a->lse && !aligned(a->lse, 4)) return FMHA_ERR_INVALID_ARG;
-  if (a->o_stride_tok < 0 || a->o_stride_head < 0 || (a->o_stride_tok * ob) % (2 * ob) ||
-      (a->o_stride_head * ob) % (2 * ob) || (!vq && (a->o_stride_batch < 0 || a->o_stride_batch % 2)))
+  if (a->o_stride_tok < 0 || a->o_stride_head < 0 || a->o_stride_tok % 4 || a->o_stride_head % 4 ||
+      (!vq && (a->o_stride_batch < 0 || a->o_stride_batch % 4)))
     return FMHA_ERR_INVALID_ARG;
-  if ((sq_max * a->num_heads_q + 3) / 4 * a->batch >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
+  if (sq_max * a->num_heads_q * a->batch >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
   CombineParams c;
   memset(&c, 0, sizeof(c));
   c.o_part = a->o_part;

@@ -66,7 +66,7 @@ struct FwdKernel {
   int dv;
   int nwm;   // waves along query rows (16 rows each)
   int nwk;   // waves splitting the key block
-  int bn;    // keys per wave per iteration
+  int bn;    // keys per wave per iteration (0: decode kernel, 32 keys per wave)
   int id;
   FwdLaunchFn launch;
 };
@@ -76,6 +76,11 @@ const FwdKernel* registry_f32(int* n);
 const FwdKernel* registry_f16(int* n);
 const FwdKernel* registry_bf16(int* n);
 const FwdKernel* registry_fp8(int* n);
+// Decode kernels (one 16-row tile, waves stream disjoint key ranges).
+const FwdKernel* registry_f32_decode(int* n);
+const FwdKernel* registry_f16_decode(int* n);
+const FwdKernel* registry_bf16_decode(int* n);
+const FwdKernel* registry_fp8_decode(int* n);
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 

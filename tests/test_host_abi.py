@@ -146,8 +146,12 @@ def test_misaligned_pointer_and_stride():
 
 def test_null_pointers_rejected_unless_empty():
     a = make()
-    a.out = None
+    a.q = None
     assert check(a)[0] == INVALID
+    a = make(splits=1)
+    a.out = None  # partials-only check: accepted only with a split
+    assert check(a)[0] == OK
+    assert fmha.lib.fmha_fwd_splitkv_partials(ctypes.byref(a), None) == INVALID
     a = make(batch=0)
     a.out = a.q = a.k = a.v = None
     assert check(a)[0] == OK
