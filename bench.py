@@ -38,7 +38,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8_e4m3": 5000.0, "f32": 157.3}
 ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fmha_fwd_kernel.h", "fmha_params.h", "fmha_combine.hip", "fmha_host.cpp"]
+KERNEL_SOURCES = ["fmha_fwd_kernel.h", "fmha_decode_kernel.h", "fmha_params.h", "fmha_combine.hip",
+                  "fmha_host.cpp", "fmha_fwd_bf16.hip", "fmha_fwd_f16.hip", "fmha_fwd_fp8.hip",
+                  "fmha_fwd_f32.hip"]
 
 
 # ---- workloads (shapes only; tensors come from fmha_synth) -----------------
@@ -327,7 +329,58 @@ def load_traffic(name):
     return t.get("bytes_per_launch")
 
 
+def summarize_pmc(fetch_csv, write_csv, workload, kernel_substr, copy_bytes):
+    """Per-launch HBM bytes of the dominant kernel from two rocprofv3 --pmc runs.
+
+    FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the
+    same counter reads for the plain device copy of ``copy_bytes`` bytes that
+    bench.py --copy-calibration-gib runs in the same process.  Writes the
+    result (with a hash of the kernel sources) into profiles/traffic.json.
+    """
+    import csv
+
+    def read(path):
+        rows = list(csv.DictReader(open(path)))
+        kern = [float(r["Counter_Value"]) for r in rows if kernel_substr in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 0.25 * copy_bytes / 1024]
+        if not kern or len(copies) != 1:
+            raise SystemExit(f"{path}: found {len(kern)} kernel and {len(copies)} calibration dispatches")
+        return sum(kern) / len(kern), copies[0], len(kern)
+
+    f_k, f_c, n = read(fetch_csv)
+    w_k, w_c, _ = read(write_csv)
+    f_scale, w_scale = copy_bytes / (f_c * 1024), copy_bytes / (w_c * 1024)
+    fetch_b, write_b = f_k * 1024 * f_scale, w_k * 1024 * w_scale
+    entry = dict(kernel_src_sha=kernel_source_hash(), kernel=kernel_substr, dispatches=n,
+                 fetch_kib_raw=round(f_k, 3), write_kib_raw=round(w_k, 3),
+                 copy_bytes=copy_bytes, copy_fetch_kib_raw=f_c, copy_write_kib_raw=w_c,
+                 fetch_scale=round(f_scale, 5), write_scale=round(w_scale, 5),
+                 fetch_bytes=int(fetch_b), write_bytes=int(write_b),
+                 bytes_per_launch=int(fetch_b + write_b),
+                 alg_bytes=alg_bytes(workloads()[workload]))
+    data = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    data[workload] = entry
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(entry, indent=1))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        sp = argparse.ArgumentParser()
+        sp.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+        sp.add_argument("--workload", default="long_decode")
+        sp.add_argument("--kernel", default="fmha_decode_kernel")
+        sp.add_argument("--copy-bytes", type=int, default=1 << 30)
+        a = sp.parse_args()
+        summarize_pmc(*a.summarize_pmc, a.workload, a.kernel, a.copy_bytes)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -376,7 +429,8 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = load_traffic(w["name"])
     roof["kernel_us"] = round(ms_kern * 1e3, 2)
-    roof["kernel"] = "fmha_fwd_kernel" + (" (split partials)" if r.split else "")
+    roof["kernel"] = (("fmha_decode_kernel" if r.plan.kernel_id % 1000 >= 100 else "fmha_fwd_kernel")
+                      + (" (split partials)" if r.split else ""))
 
     others = []
     if not args.no_others:
