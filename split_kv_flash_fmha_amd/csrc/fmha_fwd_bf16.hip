@@ -1,6 +1,7 @@
 // Compiled attention kernel instances for bf16 inputs (generated list;
 // edit here and in the host's selection rules together).
 #include "fmha_decode_kernel.h"
+#include "fmha_prefill_kernel.h"
 #include "fmha_fwd_kernel.h"
 
 namespace fmha {
@@ -42,6 +43,20 @@ static const FwdKernel kDecTable[] = {
 const FwdKernel* registry_bf16_decode(int* n) {
   *n = (int)(sizeof(kDecTable) / sizeof(kDecTable[0]));
   return kDecTable;
+}
+
+// Prefill instances (32x32 MFMA tiles, 4 waves x 32 rows, 64 keys per iteration).
+#define FMHA_PF(D, ID) \
+  {DT_BF16, D, D, 4, 1, 64, ID, &launch_prefill<PfCfg<DT_BF16, D, 4, 64>>}
+
+static const FwdKernel kPfTable[] = {
+    FMHA_PF(64, 200),
+    FMHA_PF(128, 201),
+};
+
+const FwdKernel* registry_bf16_prefill(int* n) {
+  *n = (int)(sizeof(kPfTable) / sizeof(kPfTable[0]));
+  return kPfTable;
 }
 
 }  // namespace fmha

@@ -31,4 +31,10 @@ const FwdKernel* registry_f32_decode(int* n) {
   return nullptr;
 }
 
+// No 32x32-tile prefill instances for f32 inputs (the 16-row kernel serves them).
+const FwdKernel* registry_f32_prefill(int* n) {
+  *n = 0;
+  return nullptr;
+}
+
 }  // namespace fmha

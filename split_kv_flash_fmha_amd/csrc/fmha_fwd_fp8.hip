@@ -40,4 +40,10 @@ const FwdKernel* registry_fp8_decode(int* n) {
   return kDecTable;
 }
 
+// No 32x32-tile prefill instances for fp8 inputs (the 16-row kernel serves them).
+const FwdKernel* registry_fp8_prefill(int* n) {
+  *n = 0;
+  return nullptr;
+}
+
 }  // namespace fmha

@@ -68,6 +68,24 @@ const FwdKernel* decode_registry(int dt, int* n) {
   }
 }
 
+const FwdKernel* prefill_registry(int dt, int* n) {
+  switch (dt) {
+    case FMHA_DTYPE_F32: return registry_f32_prefill(n);
+    case FMHA_DTYPE_F16: return registry_f16_prefill(n);
+    case FMHA_DTYPE_BF16: return registry_bf16_prefill(n);
+    case FMHA_DTYPE_FP8_E4M3: return registry_fp8_prefill(n);
+    default: *n = 0; return nullptr;
+  }
+}
+
+const FwdKernel* find_prefill(int dt, int dqk, int dv) {
+  int n = 0;
+  const FwdKernel* t = prefill_registry(dt, &n);
+  for (int i = 0; i < n; ++i)
+    if (t[i].dqk == dqk && t[i].dv == dv) return &t[i];
+  return nullptr;
+}
+
 const FwdKernel* find_decode(int dt, int dqk, int dv) {
   int n = 0;
   const FwdKernel* t = decode_registry(dt, &n);
@@ -182,13 +200,20 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   const int G = a->num_heads_q / a->num_heads_kv;
   int nwm = 1, nwk = 4;
   pick_shape(r->sq_max * G, &nwm, &nwk);
+  // kernel family by query rows per (sequence, kv head): decode (<= 16),
+  // 16-row tiles (<= 80), 32x32-tile prefill (more), with fallbacks
   const FwdKernel* kern = nullptr;
+  bool prefill = false;
   if (r->sq_max * G <= 16) kern = find_decode(a->in_dtype, a->head_dim_qk, a->head_dim_v);
+  if (!kern && r->sq_max * G > 80) {
+    kern = find_prefill(a->in_dtype, a->head_dim_qk, a->head_dim_v);
+    prefill = kern != nullptr;
+  }
   if (!kern) kern = find_kernel(a->in_dtype, a->head_dim_qk, a->head_dim_v, nwm, nwk);
   if (!kern) return FMHA_ERR_UNSUPPORTED;
   r->kernel = kern;
   pl.kernel_id = a->in_dtype * 1000 + kern->id;
-  pl.rows_per_tile = 16 * kern->nwm;
+  pl.rows_per_tile = (prefill ? 32 : 16) * kern->nwm;
   // decode kernels stream 32-key blocks per wave; splits are cut in multiples of that
   pl.key_block = kern->bn > 0 ? kern->nwk * kern->bn : 32;
   const int64_t rows = r->sq_max * G;

@@ -81,6 +81,11 @@ const FwdKernel* registry_f32_decode(int* n);
 const FwdKernel* registry_f16_decode(int* n);
 const FwdKernel* registry_bf16_decode(int* n);
 const FwdKernel* registry_fp8_decode(int* n);
+// Prefill kernels (32x32 MFMA tiles, 32 rows per wave).
+const FwdKernel* registry_f32_prefill(int* n);
+const FwdKernel* registry_f16_prefill(int* n);
+const FwdKernel* registry_bf16_prefill(int* n);
+const FwdKernel* registry_fp8_prefill(int* n);
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 

@@ -1,0 +1,353 @@
+// Prefill kernel for gfx950: many query rows per (sequence, kv head), so the
+// work is a dense contraction on MFMA.  One workgroup = NWM waves x 32 query
+// rows; per iteration it stages BN keys of K and V in LDS and every wave runs
+//   S^T[key, row] = K Q^T       (v_mfma_f32_32x32x16_{f16,bf16}, A = K, B = Q^T)
+//   O^T[dv, row] += V^T P^T     (A = V^T via ds_read_b64_tr_b16, B = P^T)
+// with the online exp2 softmax in between (flash attention forward; web pages
+// on split-KV flash attention: "Adds variable sequence lengths to the Hopper
+// CuTe DSL FMHA example", sections Implementation and Performance, for the
+// varlen grid, masks and row-predicated stores).
+//
+// 32x32 tiles halve the LDS bytes read per MFMA flop compared with 16x16
+// tiles (each K/V fragment feeds 32 query rows).  In the 32x32 output layout
+// lane l owns query row l%32 and 16 of the 32 keys of a tile (the other 16
+// sit in lane l^32), so a row reduction is 15 local steps plus one exchange
+// with the partner lane, and P^T feeds the second MFMA from registers.
+//
+// K and V blocks move HBM -> LDS with gfx950's direct-to-LDS loads (16 bytes
+// per lane, no register staging), rows unpadded with an XOR chunk swizzle
+// that keeps both the 16-byte K reads and the V transpose reads free of bank
+// conflicts.  The LDS holds two key blocks: block n+1 is in flight while
+// block n is computed, one barrier per block.
+//
+// Softmax bookkeeping uses a lazily moved reference max per row: p =
+// exp2(scale*s - m_ref) with m_ref moved (and O, l rescaled by
+// exp2(m_ref_old - m_ref_new)) only when some row's running max exceeds its
+// m_ref by more than kRescaleSlack (log2 units).  O and l are accumulated
+// against the same m_ref, so O = acc / l and LSE = m_ref + log2 l are exact;
+// p <= 2^kRescaleSlack keeps fp16/bf16 P in range.
+#pragma once
+#include "fmha_decode_kernel.h"
+#include "fmha_fwd_kernel.h"
+
+namespace fmha {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(f32x16 acc, u32x4 a, u32x4 b) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc,
+                                                  0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   acc, 0, 0, 0);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_in(float a, float b) {
+  if constexpr (DT == DT_F16)
+    return pack_f16x2(a, b);
+  else
+    return pack_bf16x2(a, b);
+}
+
+constexpr float kRescaleSlack = 8.0f;
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_p(float a, float b) {
+  if constexpr (DT == DT_F16) {
+    // P in [0, 2^8]: round-toward-zero packing costs one instruction per pair
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  } else {
+    return pack_bf16x2(a, b);
+  }
+}
+
+template <int DT_, int D_, int NWM_, int BN_>
+struct PfCfg {
+  static constexpr int DT = DT_;
+  static constexpr int D = D_;          // Dqk == Dv
+  static constexpr int NWM = NWM_;      // waves, 32 rows each
+  static constexpr int BN = BN_;        // keys per iteration
+  static constexpr int NTHR = 64 * NWM;
+  static constexpr int ROWS = 32 * NWM;
+  static constexpr int KS = D / 16;     // k-steps of QK (16 d each)
+  static constexpr int NT = BN / 32;    // S^T tiles (32 keys each)
+  static constexpr int TV = D / 32;     // O^T tiles (32 dv each)
+  static constexpr int ROWB = D * 2;    // bytes per K / V row (unpadded, swizzled)
+  static constexpr int RPL = 1024 / ROWB;          // rows per 1 KiB direct-to-LDS load
+  static constexpr int TILE = BN * ROWB;           // one K or V block
+  static constexpr int LOADS = 2 * TILE / 1024;    // 1 KiB loads per K+V block
+  static constexpr int LPW = LOADS / NWM;          // per wave
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int LDS = 2 * STAGE;            // double buffered
+  static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
+  static_assert(1024 % ROWB == 0 && LOADS % NWM == 0, "whole 1 KiB loads per wave");
+};
+
+// 16-byte chunk c of row r sits at chunk slot c ^ swz(r) (an involution on
+// the low bits, so a row keeps its 128-byte halves).  K: 8 consecutive rows
+// read at one chunk land in 8 distinct slots of a 128-byte bank window.  V:
+// 4 consecutive rows x 2 adjacent chunks (one transpose read of a 16-lane
+// group) land in 8 distinct slots.
+__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
+
+template <class C>
+__global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
+  constexpr int DT = C::DT;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wm = tid >> 6;
+  const int hl = lane >> 5;   // lane half: contraction slots / output row group
+  const int lr = lane & 31;   // query row within the wave / MFMA column
+
+  int64_t bid = blockIdx.x;
+  const int S = p.num_splits;
+  const int split = (int)(bid % S);
+  bid /= S;
+  const int hkv = (int)(bid % p.hkv);
+  bid /= p.hkv;
+  const int b = (int)(bid % p.batch);
+  bid /= p.batch;
+  const int qtile = p.num_q_tiles - 1 - (int)bid;
+
+  int q_off, sq, k_off, sk;
+  if (p.cu_q) {
+    q_off = p.cu_q[b];
+    sq = p.cu_q[b + 1] - q_off;
+  } else {
+    q_off = b * p.seqlen_q;
+    sq = p.seqlen_q;
+  }
+  if (p.cu_k) {
+    k_off = p.cu_k[b];
+    sk = p.cu_k[b + 1] - k_off;
+  } else {
+    k_off = b * p.seqlen_k;
+    sk = p.seqlen_k;
+  }
+  const int G = p.group;
+  const int rows = sq * G;
+  const int row0 = qtile * C::ROWS;
+  if (row0 >= rows || sk <= 0) return;
+  const int kb = split * p.chunk;
+  if (kb >= sk) return;
+  const int ke = S > 1 ? min(kb + p.chunk, sk) : sk;
+
+  const char* kbase = p.k + (p.cu_k ? (int64_t)k_off * p.k_st : (int64_t)b * p.k_sb) + (int64_t)hkv * p.k_sh;
+  const char* vbase = p.v + (p.cu_k ? (int64_t)k_off * p.v_st : (int64_t)b * p.v_sb) + (int64_t)hkv * p.v_sh;
+
+  const int r = row0 + 32 * wm + lr;
+  const bool row_ok = r < rows;
+  const int iq = row_ok ? r / G : 0;
+  const int hq = hkv * G + (row_ok ? r % G : 0);
+
+  // Q^T (B operand): k-step s, lane half h holds d = 16s + 8h .. +8
+  u32x4 qf[C::KS];
+  {
+    const char* qrow = p.q + (p.cu_q ? (int64_t)(q_off + iq) * p.q_st : (int64_t)b * p.q_sb + (int64_t)iq * p.q_st) +
+                       (int64_t)hq * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qf[s] = row_ok ? *(const u32x4*)(qrow + (16 * s + 8 * hl) * 2) : z;
+    }
+  }
+  const float scale_log2 = p.scale_log2;
+
+  const int shift = sk - sq;
+  auto lo_of = [&](int i) { return p.wl >= 0 ? max(i + shift - p.wl, 0) : 0; };
+  auto hi_of = [&](int i) { return p.wr >= 0 ? min(i + shift + p.wr, sk - 1) : sk - 1; };
+  const int last_row = min(row0 + C::ROWS, rows) - 1;
+  const int iq_lo = row0 / G, iq_hi = last_row / G;
+  const int tile_lo = max(kb, lo_of(iq_lo));
+  const int tile_hi = min(ke - 1, hi_of(iq_hi));
+  const int full_lo = max(kb, lo_of(iq_hi));
+  const int full_hi = min(ke - 1, hi_of(iq_lo));
+  const int my_lo = max(kb, lo_of(iq));
+  const int my_hi = min(ke - 1, hi_of(iq));
+  const int j_begin = (tile_lo / C::BN) * C::BN;
+  const int j_end = tile_hi + 1;
+  const int n_iter = j_end > j_begin ? (j_end - j_begin + C::BN - 1) / C::BN : 0;
+
+  f32x16 acc[C::TV];
+#pragma unroll
+  for (int t = 0; t < C::TV; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // One key block = LOADS direct-to-LDS loads of 1 KiB (RPL rows each): wave
+  // wm issues loads [wm*LPW, (wm+1)*LPW); K loads first, then V.  Lane l of a
+  // load writes LDS bytes [16l, 16l+16) of it, i.e. slot l % (ROWB/16) of row
+  // l / (ROWB/16), so it fetches the chunk that belongs in that slot.  Rows past
+  // the key range re-read the last valid row (finite data, masked to p = 0).
+  auto issue_block = [&](int j0, int stage) {
+    char* base = smem + stage * C::STAGE;
+#pragma unroll
+    for (int n = 0; n < C::LPW; ++n) {
+      const int ld = wm * C::LPW + n;
+      const bool is_v = ld * 1024 >= C::TILE;
+      const int lrow = (ld * 1024 - (is_v ? C::TILE : 0)) / C::ROWB + lane / (C::ROWB / 16);
+      const int slot = lane % (C::ROWB / 16);
+      const int chunk = is_v ? v_slot(lrow, slot) : k_slot(lrow, slot);
+      const int j = min(j0 + lrow, ke - 1);
+      const char* src = (is_v ? vbase + (int64_t)j * p.v_st : kbase + (int64_t)j * p.k_st) + chunk * 16;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(base + ld * 1024), 16, 0, 0);
+    }
+  };
+
+  const int e4 = (lane >> 2) & 3, jq = lane & 3, grp = (lane >> 4) & 1;
+  if (n_iter > 0) issue_block(j_begin, 0);
+  for (int it = 0; it < n_iter; ++it) {
+    const int j0 = j_begin + it * C::BN;
+    // this wave's loads of block it have landed; the barrier makes every
+    // wave's part visible and retires all reads of the other stage
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 < n_iter) issue_block(j0 + C::BN, (it + 1) & 1);
+    const char* Ks = smem + (it & 1) * C::STAGE;
+    const char* Vs = Ks + C::TILE;
+
+    // S^T tiles: lane (hl, row) holds keys 32u + 8j + 4hl + i in register 4j + i
+    f32x16 s[C::NT];
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < C::KS; ++k) {
+      u32x4 kf[C::NT];
+#pragma unroll
+      for (int u = 0; u < C::NT; ++u) {
+        const int row = 32 * u + lr;
+        kf[u] = *(const u32x4*)(Ks + row * C::ROWB + k_slot(row, 2 * k + hl) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < C::NT; ++u) s[u] = mfma32<DT>(s[u], kf[u], qf[k]);
+    }
+
+    const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
+    if (!full) {
+#pragma unroll
+      for (int u = 0; u < C::NT; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + 32 * u + 8 * (e >> 2) + 4 * hl + (e & 3);
+          if (j < my_lo || j > my_hi) s[u][e] = -INFINITY;
+        }
+    }
+    // raw row max (scale > 0 commutes with max), one exchange with lane ^ 32
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_blk = mx * scale_log2;
+    // move the reference max only when some row ran ahead of it by > slack
+    if (__any(m_blk > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < C::TV; ++t) acc[t] *= alpha;
+      m_run = m_new;
+    }
+    const float nbase = -(m_run == -INFINITY ? 0.f : m_run);
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(__builtin_fmaf(s[u][e], scale_log2, nbase));
+        s[u][e] = pe;
+        rs += pe;
+      }
+    }
+    l_run += rs;
+    // O^T += V^T P^T, 16 keys per MFMA: tile u, half m covers keys 32u+16m+{0..15}
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        u32x4 pf;
+        pf.x = pack2_p<DT>(s[u][8 * m + 0], s[u][8 * m + 1]);
+        pf.y = pack2_p<DT>(s[u][8 * m + 2], s[u][8 * m + 3]);
+        pf.z = pack2_p<DT>(s[u][8 * m + 4], s[u][8 * m + 5]);
+        pf.w = pack2_p<DT>(s[u][8 * m + 6], s[u][8 * m + 7]);
+        // lane 4e+jq of 16-lane group (hl, grp) reads row 32u+16m+8q+4hl+e,
+        // columns 32t+16grp+4jq..+3; it receives column lr of those 4 rows
+        u32x4 vf[C::TV];
+#pragma unroll
+        for (int t = 0; t < C::TV; ++t) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int row = 32 * u + 16 * m + 8 * q + 4 * hl + e4;
+            const int chunk = 4 * t + 2 * grp + (jq >> 1);
+            const char* a = Vs + row * C::ROWB + v_slot(row, chunk) * 16 + 8 * (jq & 1);
+            const i32x2 x = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a)));
+            if (q == 0) {
+              vf[t].x = (uint32_t)x.x;
+              vf[t].y = (uint32_t)x.y;
+            } else {
+              vf[t].z = (uint32_t)x.x;
+              vf[t].w = (uint32_t)x.y;
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < C::TV; ++t) acc[t] = mfma32<DT>(acc[t], vf[t], pf);
+      }
+    }
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const bool live = l_tot > 0.f;
+  const float inv = live ? 1.0f / l_tot : 0.f;
+  const float lse_v = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (S > 1) {
+    const int64_t tglob = (int64_t)q_off + iq;
+    float* op = p.o_part + (((int64_t)split * p.total_q + tglob) * p.hq + hq) * C::D;
+#pragma unroll
+    for (int t = 0; t < C::TV; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 o = {acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv, acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv};
+        *(f32x4*)(op + 32 * t + 8 * j + 4 * hl) = o;
+      }
+    if (hl == 0) p.lse_part[((int64_t)split * p.hq + hq) * p.total_q + tglob] = lse_v;
+  } else {
+    char* op = p.o + (p.cu_q ? (int64_t)(q_off + iq) * p.o_st : (int64_t)b * p.o_sb + (int64_t)iq * p.o_st) +
+               (int64_t)hq * p.o_sh;
+#pragma unroll
+    for (int t = 0; t < C::TV; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w = {pack2_in<DT>(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
+                   pack2_in<DT>(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
+        *(u32x2*)(op + (32 * t + 8 * j + 4 * hl) * 2) = w;
+      }
+    if (p.lse && hl == 0) {
+      const int64_t li = p.cu_q ? (int64_t)hq * p.lse_sh + q_off + iq : (int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + iq;
+      p.lse[li] = lse_v;
+    }
+  }
+}
+
+template <class C>
+hipError_t launch_prefill(const FwdParams& p, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL(fmha_prefill_kernel<C>, dim3((uint32_t)grid), dim3(C::NTHR), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fmha
