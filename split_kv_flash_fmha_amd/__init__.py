@@ -94,7 +94,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first "
-            "(python -m split_kv_flash_fmha_amd.build)")
+            "(python split_kv_flash_fmha_amd/build.py)")
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     L.fmha_fwd_check.argtypes = [P(FwdArgs), P(Plan)]

@@ -1,6 +1,9 @@
 """Build libfmha.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m split_kv_flash_fmha_amd.build [--jobs N]
+    python split_kv_flash_fmha_amd/build.py [--jobs N]
+
+(run it by path: importing the package loads libfmha.so, which is what is
+being built)
 
 Each translation unit is compiled to an object under _build/ in parallel and
 the objects are linked into split_kv_flash_fmha_amd/libfmha.so.
@@ -64,6 +67,12 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    # a kernel whose host-side launch stub the compiler dropped shows up only
+    # as an undefined symbol at load time: refuse such a library here
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the link: " + ", ".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)

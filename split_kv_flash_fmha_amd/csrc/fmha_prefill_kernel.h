@@ -14,10 +14,10 @@
 // sit in lane l^32), so a row reduction is 15 local steps plus one exchange
 // with the partner lane, and P^T feeds the second MFMA from registers.
 //
-// K and V blocks move HBM -> LDS with gfx950's direct-to-LDS loads (16 bytes
-// per lane, no register staging), rows unpadded with an XOR chunk swizzle
-// that keeps both the 16-byte K reads and the V transpose reads free of bank
-// conflicts.  The LDS holds two key blocks: block n+1 is in flight while
+// K and V blocks move HBM -> LDS with buffer loads that write LDS directly
+// (16 bytes per lane, no register staging), rows unpadded with an XOR chunk
+// swizzle that keeps both the 16-byte K reads and the V transpose reads free
+// of bank conflicts.  The LDS holds two key blocks: block n+1 is in flight while
 // block n is computed, one barrier per block.
 //
 // Softmax bookkeeping uses a lazily moved reference max per row: p =
@@ -84,16 +84,34 @@ struct PfCfg {
   static constexpr int STAGE = 2 * TILE;
   static constexpr int LDS = 2 * STAGE;            // double buffered
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
-  static_assert(1024 % ROWB == 0 && LOADS % NWM == 0, "whole 1 KiB loads per wave");
+  static_assert(1024 % ROWB == 0 && LOADS % (2 * NWM) == 0, "whole 1 KiB K and V loads per wave");
 };
 
-// 16-byte chunk c of row r sits at chunk slot c ^ swz(r) (an involution on
-// the low bits, so a row keeps its 128-byte halves).  K: 8 consecutive rows
-// read at one chunk land in 8 distinct slots of a 128-byte bank window.  V:
-// 4 consecutive rows x 2 adjacent chunks (one transpose read of a 16-lane
-// group) land in 8 distinct slots.
-__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & 7); }
-__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
+// 16-byte chunk c of row r sits at chunk slot c ^ swz(r) (an XOR on the low
+// bits, so it is its own inverse).  Chosen so that both LDS read patterns are
+// free of bank conflicts whether the LDS serves 128 or 256 bytes per pass:
+//  * K (16-byte A-operand reads): 16 consecutive rows at one chunk;
+//  * V (transpose reads): 4 consecutive rows x 4 adjacent chunks per 32 lanes.
+template <int ROWB>
+__device__ __forceinline__ int k_slot(int r, int c) {
+  if constexpr (ROWB >= 256) return c ^ (r & 15);
+  else return c ^ ((r ^ (r >> 3)) & 7);
+}
+template <int ROWB>
+__device__ __forceinline__ int v_slot(int r, int c) {
+  const int e = r & 3;
+  if constexpr (ROWB >= 256) return c ^ (4 * e + 2 * (e >> 1));
+  else return c ^ (2 * e);
+}
+
+// One 16-byte-per-lane buffer load that writes LDS at lds + 16 * lane.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nbytes, 0x00020000);
+}
 
 template <class C>
 __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
@@ -183,56 +201,98 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // One key block = LOADS direct-to-LDS loads of 1 KiB (RPL rows each): wave
-  // wm issues loads [wm*LPW, (wm+1)*LPW); K loads first, then V.  Lane l of a
+  // One key block = LOADS buffer->LDS loads of 1 KiB (RPL rows each): wave wm
+  // issues loads [wm*LPW, (wm+1)*LPW), K loads first, then V.  Lane l of a
   // load writes LDS bytes [16l, 16l+16) of it, i.e. slot l % (ROWB/16) of row
-  // l / (ROWB/16), so it fetches the chunk that belongs in that slot.  Rows past
-  // the key range re-read the last valid row (finite data, masked to p = 0).
-  auto issue_block = [&](int j0, int stage) {
+  // l / (ROWB/16), so it fetches the chunk that belongs in that slot.  Its
+  // byte offset from the block's first row is a loop constant; the block base
+  // goes into the buffer descriptor, whose size ends at the last valid key, so
+  // rows past the key range read as zero.
+  constexpr int CPR = C::ROWB / 16;  // chunks per row
+  // wave wm loads rows [wm * LPW/2 * RPL, ...) of the K tile and of the V tile
+  int kld_off[C::LPW / 2], vld_off[C::LPW / 2];
+#pragma unroll
+  for (int n = 0; n < C::LPW / 2; ++n) {
+    const int lrow = (wm * C::LPW / 2 + n) * C::RPL + lane / CPR;
+    kld_off[n] = lrow * (int)p.k_st + k_slot<C::ROWB>(lrow, lane % CPR) * 16;
+    vld_off[n] = lrow * (int)p.v_st + v_slot<C::ROWB>(lrow, lane % CPR) * 16;
+  }
+  // LDS read offsets (bytes within a stage's K / V tile), loop constants
+  int koff[C::NT][C::KS];
+#pragma unroll
+  for (int u = 0; u < C::NT; ++u)
+#pragma unroll
+    for (int k = 0; k < C::KS; ++k) {
+      const int row = 32 * u + lr;
+      koff[u][k] = row * C::ROWB + k_slot<C::ROWB>(row, 2 * k + hl) * 16;
+    }
+  const int e4 = (lane >> 2) & 3, jq = lane & 3, grp = (lane >> 4) & 1;
+  int voff[C::TV];  // + (32u + 16m + 8q) * ROWB per read (row & 3 == e4 throughout)
+#pragma unroll
+  for (int t = 0; t < C::TV; ++t)
+    voff[t] = (4 * hl + e4) * C::ROWB + v_slot<C::ROWB>(e4, 4 * t + 2 * grp + (jq >> 1)) * 16 + 8 * (jq & 1);
+
+  // zero both stages once so no slot is ever read uninitialised
+#pragma unroll
+  for (int i = tid * 16; i < C::LDS; i += C::NTHR * 16) *(u32x4*)(smem + i) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  // K and V of block b live in K stage b%2 / V stage b%2.  K runs one block
+  // ahead of V: during iteration it the loads of K(it+2) and V(it+1) are in
+  // flight while QK(it+1) and PV(it) are computed.
+  auto issue_k = [&](int j0, int stage) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)j0 * p.k_st, (int64_t)(ke - 1 - j0) * p.k_st + C::ROWB);
     char* base = smem + stage * C::STAGE;
 #pragma unroll
-    for (int n = 0; n < C::LPW; ++n) {
-      const int ld = wm * C::LPW + n;
-      const bool is_v = ld * 1024 >= C::TILE;
-      const int lrow = (ld * 1024 - (is_v ? C::TILE : 0)) / C::ROWB + lane / (C::ROWB / 16);
-      const int slot = lane % (C::ROWB / 16);
-      const int chunk = is_v ? v_slot(lrow, slot) : k_slot(lrow, slot);
-      const int j = min(j0 + lrow, ke - 1);
-      const char* src = (is_v ? vbase + (int64_t)j * p.v_st : kbase + (int64_t)j * p.k_st) + chunk * 16;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(base + ld * 1024), 16, 0, 0);
-    }
+    for (int n = 0; n < C::LPW / 2; ++n) buffer_to_lds16(rk, base + (wm * C::LPW / 2 + n) * 1024, kld_off[n]);
   };
-
-  const int e4 = (lane >> 2) & 3, jq = lane & 3, grp = (lane >> 4) & 1;
-  if (n_iter > 0) issue_block(j_begin, 0);
-  for (int it = 0; it < n_iter; ++it) {
-    const int j0 = j_begin + it * C::BN;
-    // this wave's loads of block it have landed; the barrier makes every
-    // wave's part visible and retires all reads of the other stage
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < n_iter) issue_block(j0 + C::BN, (it + 1) & 1);
-    const char* Ks = smem + (it & 1) * C::STAGE;
-    const char* Vs = Ks + C::TILE;
-
-    // S^T tiles: lane (hl, row) holds keys 32u + 8j + 4hl + i in register 4j + i
-    f32x16 s[C::NT];
+  auto issue_v = [&](int j0, int stage) {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)j0 * p.v_st, (int64_t)(ke - 1 - j0) * p.v_st + C::ROWB);
+    char* base = smem + stage * C::STAGE + C::TILE;
+#pragma unroll
+    for (int n = 0; n < C::LPW / 2; ++n) buffer_to_lds16(rv, base + (wm * C::LPW / 2 + n) * 1024, vld_off[n]);
+  };
+  auto qk = [&](f32x16 (&sd)[C::NT], int stage) {
+    const char* Ks = smem + stage * C::STAGE;
 #pragma unroll
     for (int u = 0; u < C::NT; ++u)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sd[u][e] = 0.f;
 #pragma unroll
     for (int k = 0; k < C::KS; ++k) {
       u32x4 kf[C::NT];
 #pragma unroll
-      for (int u = 0; u < C::NT; ++u) {
-        const int row = 32 * u + lr;
-        kf[u] = *(const u32x4*)(Ks + row * C::ROWB + k_slot(row, 2 * k + hl) * 16);
-      }
+      for (int u = 0; u < C::NT; ++u) kf[u] = *(const u32x4*)(Ks + koff[u][k]);
 #pragma unroll
-      for (int u = 0; u < C::NT; ++u) s[u] = mfma32<DT>(s[u], kf[u], qf[k]);
+      for (int u = 0; u < C::NT; ++u) sd[u] = mfma32<DT>(sd[u], kf[u], qf[k]);
     }
+  };
+
+  f32x16 s_cur[C::NT], s_nxt[C::NT];
+  if (n_iter > 0) {
+    issue_k(j_begin, 0);
+    issue_v(j_begin, 0);
+    if (n_iter > 1) issue_k(j_begin + C::BN, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(s_cur, 0);
+  }
+
+  // ST = it % 2, passed as a literal at both call sites so the stage offsets
+  // fold into the LDS instructions' immediate offsets after inlining
+  auto body = [&](const int ST, int it) {
+    const int j0 = j_begin + it * C::BN;
+    // loads of K(it+1) and V(it) have landed everywhere, and every wave is done
+    // with K stage ST (QK(it)) and V stage ST^1 (PV(it-1))
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 2 < n_iter) issue_k(j0 + 2 * C::BN, ST);
+    if (it + 1 < n_iter) issue_v(j0 + C::BN, ST ^ 1);
+    // QK of the next block goes to the MFMA pipe while this block's softmax
+    // runs on the VALU
+    if (it + 1 < n_iter) qk(s_nxt, ST ^ 1);
+    const char* Vs = smem + ST * C::STAGE + C::TILE;
+    f32x16 (&s)[C::NT] = s_cur;
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
     if (!full) {
@@ -290,9 +350,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
         for (int t = 0; t < C::TV; ++t) {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const int row = 32 * u + 16 * m + 8 * q + 4 * hl + e4;
-            const int chunk = 4 * t + 2 * grp + (jq >> 1);
-            const char* a = Vs + row * C::ROWB + v_slot(row, chunk) * 16 + 8 * (jq & 1);
+            const char* a = Vs + (32 * u + 16 * m + 8 * q) * C::ROWB + voff[t];
             const i32x2 x = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a)));
             if (q == 0) {
               vf[t].x = (uint32_t)x.x;
@@ -307,6 +365,13 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
         for (int t = 0; t < C::TV; ++t) acc[t] = mfma32<DT>(acc[t], vf[t], pf);
       }
     }
+#pragma unroll
+    for (int u = 0; u < C::NT; ++u) s_cur[u] = s_nxt[u];
+  };
+
+  for (int it = 0; it < n_iter; it += 2) {
+    body(0, it);
+    if (it + 1 < n_iter) body(1, it + 1);
   }
 
   // ---- epilogue
