@@ -1,6 +1,7 @@
 // Compiled attention kernel instances for fp8 inputs (generated list;
 // edit here and in the host's selection rules together).
 #include "fmha_decode_kernel.h"
+#include "fmha_prefill8_kernel.h"
 #include "fmha_fwd_kernel.h"
 
 namespace fmha {
@@ -40,10 +41,21 @@ const FwdKernel* registry_fp8_decode(int* n) {
   return kDecTable;
 }
 
-// No 32x32-tile prefill instances for fp8 inputs (the 16-row kernel serves them).
+// 32x32-tile fp8 instances (32 rows per wave, 64-key blocks); nwm picked by
+// rows per (sequence, kv head).
+#define FMHA_PF8(DQK, DV, NWM, ID) \
+  {DT_FP8, DQK, DV, NWM, 1, 64, ID, &launch_prefill8<Pf8Cfg<DQK, DV, NWM>>}
+
+static const FwdKernel kPf8Table[] = {
+    FMHA_PF8(192, 128, 3, 210),
+    FMHA_PF8(192, 128, 4, 211),
+    FMHA_PF8(128, 128, 3, 212),
+    FMHA_PF8(128, 128, 4, 213),
+};
+
 const FwdKernel* registry_fp8_prefill(int* n) {
-  *n = 0;
-  return nullptr;
+  *n = (int)(sizeof(kPf8Table) / sizeof(kPf8Table[0]));
+  return kPf8Table;
 }
 
 }  // namespace fmha

@@ -78,12 +78,18 @@ const FwdKernel* prefill_registry(int dt, int* n) {
   }
 }
 
-const FwdKernel* find_prefill(int dt, int dqk, int dv) {
+// Smallest 32-row-wave instance whose tile covers `rows`, else the largest.
+const FwdKernel* find_prefill(int dt, int dqk, int dv, int64_t rows) {
   int n = 0;
   const FwdKernel* t = prefill_registry(dt, &n);
-  for (int i = 0; i < n; ++i)
-    if (t[i].dqk == dqk && t[i].dv == dv) return &t[i];
-  return nullptr;
+  const FwdKernel* fit = nullptr;
+  const FwdKernel* big = nullptr;
+  for (int i = 0; i < n; ++i) {
+    if (t[i].dqk != dqk || t[i].dv != dv) continue;
+    if (!big || t[i].nwm > big->nwm) big = &t[i];
+    if (32 * t[i].nwm >= rows && (!fit || t[i].nwm < fit->nwm)) fit = &t[i];
+  }
+  return fit ? fit : big;
 }
 
 const FwdKernel* find_decode(int dt, int dqk, int dv) {
@@ -205,8 +211,11 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   const FwdKernel* kern = nullptr;
   bool prefill = false;
   if (r->sq_max * G <= 16) kern = find_decode(a->in_dtype, a->head_dim_qk, a->head_dim_v);
-  if (!kern && r->sq_max * G > 80) {
-    kern = find_prefill(a->in_dtype, a->head_dim_qk, a->head_dim_v);
+  // fp8 takes the 32x32-tile kernel from 17 rows (its 16-row kernel stages V
+  // byte by byte); f16/bf16 from 81 rows
+  const int64_t pf_from = a->in_dtype == FMHA_DTYPE_FP8_E4M3 ? 16 : 80;
+  if (!kern && r->sq_max * G > pf_from) {
+    kern = find_prefill(a->in_dtype, a->head_dim_qk, a->head_dim_v, r->sq_max * G);
     prefill = kern != nullptr;
   }
   if (!kern) kern = find_kernel(a->in_dtype, a->head_dim_qk, a->head_dim_v, nwm, nwk);

@@ -104,7 +104,9 @@ __device__ __forceinline__ int v_slot(int r, int c) {
   else return c ^ (2 * e);
 }
 
-// One 16-byte-per-lane buffer load that writes LDS at lds + 16 * lane.
+// One 16-byte-per-lane buffer load that writes LDS at lds + 16 * lane.  The
+// descriptors cover one key block (rows past its last valid key read as 0),
+// so their 32-bit size never wraps.
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds, int voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
@@ -241,13 +243,15 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
   // ahead of V: during iteration it the loads of K(it+2) and V(it+1) are in
   // flight while QK(it+1) and PV(it) are computed.
   auto issue_k = [&](int j0, int stage) {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)j0 * p.k_st, (int64_t)(ke - 1 - j0) * p.k_st + C::ROWB);
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(kbase + (int64_t)j0 * p.k_st, (int64_t)min(ke - 1 - j0, C::BN) * p.k_st + C::ROWB);
     char* base = smem + stage * C::STAGE;
 #pragma unroll
     for (int n = 0; n < C::LPW / 2; ++n) buffer_to_lds16(rk, base + (wm * C::LPW / 2 + n) * 1024, kld_off[n]);
   };
   auto issue_v = [&](int j0, int stage) {
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)j0 * p.v_st, (int64_t)(ke - 1 - j0) * p.v_st + C::ROWB);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(vbase + (int64_t)j0 * p.v_st, (int64_t)min(ke - 1 - j0, C::BN) * p.v_st + C::ROWB);
     char* base = smem + stage * C::STAGE + C::TILE;
 #pragma unroll
     for (int n = 0; n < C::LPW / 2; ++n) buffer_to_lds16(rv, base + (wm * C::LPW / 2 + n) * 1024, vld_off[n]);
