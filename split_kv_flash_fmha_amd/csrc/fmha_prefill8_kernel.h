@@ -16,7 +16,9 @@
 //    padded by 64 bytes so the two columns of one transpose-read pass fall in
 //    different banks.
 //  * O^T += V^T P^T with V^T from ds_read_b64_tr_b8 (8 keys x 16 dv per
-//    16-lane group) and P^T stored as e4m3 of p * 2^4.  With the reference max
+//    16-lane group) and P^T stored as e4m3 of p * 2^4.
+//  * Three LDS stages for K and for V: loads run two key blocks ahead of use,
+//    and each wave waits only for the loads it issued two iterations back.  With the reference max
 //    allowed to trail the running max by at most 2^4, p * 2^4 <= 2^8 stays
 //    inside e4m3's range; the factor is divided out with the V descale.
 #pragma once
@@ -50,15 +52,16 @@ struct Pf8Cfg {
   static constexpr int VCP = BN * 16 + 64;   // V column pitch
   static constexpr int KTILE = KCOLS * KCP;
   static constexpr int VTILE = VCOLS * VCP;
-  static constexpr int LDS = 2 * KTILE + 2 * VTILE;
+  static constexpr int NS = 3;                          // LDS ring depth (K and V)
+  static constexpr int KL = (KCOLS + NWM - 1) / NWM;    // K column loads per wave per block
+  static constexpr int VL = (VCOLS + NWM - 1) / NWM;    // V column loads per wave per block
+  static constexpr int LDS = NS * (KTILE + VTILE);
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
 };
 
 template <class C>
 __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  char* kst[2] = {smem, smem + C::KTILE};
-  char* vst[2] = {smem + 2 * C::KTILE, smem + 2 * C::KTILE + C::VTILE};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,19 +161,33 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   __syncthreads();
 
   // one 1 KiB load = 16-byte column c of the 64 rows of a block (lane = row);
-  // rows past the key range read as zero (buffer size ends at the last key)
+  // rows past the key range read as zero (descriptor ends at the last key),
+  // and a block that starts past it gets an empty descriptor (nothing is
+  // fetched).  Every wave issues exactly KL K and VL V loads per block (the
+  // last column repeated where the columns do not divide evenly; identical
+  // bytes), so the loads a wave has in flight are a compile-time count.
   auto issue_k = [&](int j0, int st) {
-    const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc(kbase + (int64_t)j0 * p.k_st, (int64_t)min(ke - 1 - j0, C::BN) * p.k_st + C::DQK);
-    for (int c = wm; c < C::KCOLS; c += C::NWM) buffer_to_lds16(rk, kst[st] + c * C::KCP, lane * (int)p.k_st + c * 16);
+    const int64_t nb = j0 < j_end ? (int64_t)min(ke - 1 - j0, C::BN) * p.k_st + C::DQK : 0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)j0 * p.k_st, nb);
+    char* dst = smem + st * C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i) {
+      const int c = min(wm + i * C::NWM, C::KCOLS - 1);
+      buffer_to_lds16(rk, dst + c * C::KCP, lane * (int)p.k_st + c * 16);
+    }
   };
   auto issue_v = [&](int j0, int st) {
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(vbase + (int64_t)j0 * p.v_st, (int64_t)min(ke - 1 - j0, C::BN) * p.v_st + C::DV);
-    for (int c = wm; c < C::VCOLS; c += C::NWM) buffer_to_lds16(rv, vst[st] + c * C::VCP, lane * (int)p.v_st + c * 16);
+    const int64_t nb = j0 < j_end ? (int64_t)min(ke - 1 - j0, C::BN) * p.v_st + C::DV : 0;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)j0 * p.v_st, nb);
+    char* dst = smem + C::NS * C::KTILE + st * C::VTILE;
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) {
+      const int c = min(wm + i * C::NWM, C::VCOLS - 1);
+      buffer_to_lds16(rv, dst + c * C::VCP, lane * (int)p.v_st + c * 16);
+    }
   };
   auto qk = [&](f32x16 (&sd)[C::NT], int st) {
-    const char* Ks = kst[st] + k_rd;
+    const char* Ks = smem + st * C::KTILE + k_rd;
 #pragma unroll
     for (int u = 0; u < C::NT; ++u)
 #pragma unroll
@@ -187,24 +204,40 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
       }
     }
   };
+  // at most KL + VL of this wave's loads (one block's K and V) in flight;
+  // loads retire in order, so everything issued before them has landed
+  constexpr int kInFlight = C::KL + C::VL;
+  static_assert(kInFlight < 64, "vmcnt");
+  auto wait_older_loads = [] {
+    __builtin_amdgcn_s_waitcnt((kInFlight & 15) | ((kInFlight >> 4) << 14) | (7 << 4) | (15 << 8));
+  };
+  const uint32_t va0 = lds_addr(smem) + (uint32_t)v_rd;
 
+  // Ring of three stages: K(b) in K stage b%3, V(b) in V stage b%3.
+  // Iteration it waits for K(it+1) and V(it), issues K(it+3) and V(it+2) and
+  // computes QK(it+1) and PV(it): loads run two blocks ahead of their use.
   f32x16 s_cur[C::NT], s_nxt[C::NT];
   if (n_iter > 0) {
     issue_k(j_begin, 0);
     issue_v(j_begin, 0);
-    if (n_iter > 1) issue_k(j_begin + C::BN, 1);
-    __builtin_amdgcn_s_waitcnt(0);
+    issue_k(j_begin + C::BN, 1);
+    issue_k(j_begin + 2 * C::BN, 2);
+    issue_v(j_begin + C::BN, 1);
+    wait_older_loads();  // K(0), V(0), K(1) landed
     __syncthreads();
     qk(s_cur, 0);
   }
 
-  auto body = [&](const int ST, int it) {
+  int st = 0;  // it % 3
+  for (int it = 0; it < n_iter; ++it) {
     const int j0 = j_begin + it * C::BN;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 2 < n_iter) issue_k(j0 + 2 * C::BN, ST);
-    if (it + 1 < n_iter) issue_v(j0 + C::BN, ST ^ 1);
-    if (it + 1 < n_iter) qk(s_nxt, ST ^ 1);
+    const int st1 = st == 2 ? 0 : st + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    wait_older_loads();
+    __syncthreads();  // K(it+1), V(it) in LDS everywhere; stages of K(it), V(it-1) free
+    issue_k(j0 + 3 * C::BN, st);
+    issue_v(j0 + 2 * C::BN, st2);
+    if (it + 1 < n_iter) qk(s_nxt, st1);
     f32x16 (&s)[C::NT] = s_cur;
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
@@ -244,35 +277,46 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
       }
     }
     l_run += rs;
-    const char* Vs = vst[ST] + v_rd;
-#pragma unroll
-    for (int u = 0; u < C::NT; ++u) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float ps = kPScale8;
-        const uint32_t p0 = pack_fp8x4(s[u][8 * m + 0] * ps, s[u][8 * m + 1] * ps, s[u][8 * m + 2] * ps,
-                                       s[u][8 * m + 3] * ps);
-        const uint32_t p1 = pack_fp8x4(s[u][8 * m + 4] * ps, s[u][8 * m + 5] * ps, s[u][8 * m + 6] * ps,
-                                       s[u][8 * m + 7] * ps);
-        // lane 2e+jh of 16-lane group (hl, gq) reads key row
-        // 32u+16m+8(e/4)+4hl+e%4, dv bytes 32t+16gq+8jh..+7; it receives dv
-        // column lr of those 8 keys
-        i32x2 vf[C::TV];
-#pragma unroll
-        for (int t = 0; t < C::TV; ++t)
-          vf[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + 2 * t * C::VCP + (32 * u + 16 * m) * 16));
-#pragma unroll
-        for (int t = 0; t < C::TV; ++t) acc[t] = mfma32_fp8(acc[t], (uint32_t)vf[t].x, (uint32_t)vf[t].y, p0, p1);
+    // O^T += V^T P^T: group g = (u, m) covers keys 32u+16m+{0..15}.  Lane
+    // 2e+jh of 16-lane group (hl, gq) reads key row 32u+16m+8(e/4)+4hl+e%4,
+    // dv bytes 32t+16gq+8jh..+7, and receives dv column lr of those 8 keys.
+    // The reads of group g+1 are in flight during group g's MFMAs.
+    const uint32_t va = va0 + (uint32_t)(st * C::VTILE);
+    i32x2 vr[2][C::TV];
+    auto read_group = [&](auto G_) {
+      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
+      static_for<C::TV>([&](auto T_) {
+        constexpr int t = decltype(T_)::value;
+        vr[g & 1][t] = lds_tr8<C::NS * C::KTILE + 2 * t * C::VCP + (32 * u + 16 * m) * 16>(va);
+      });
+    };
+    read_group(int_c<0>{});
+    static_for<2 * C::NT>([&](auto G_) {
+      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
+      const float ps = kPScale8;
+      const uint32_t p0 =
+          pack_fp8x4(s[u][8 * m + 0] * ps, s[u][8 * m + 1] * ps, s[u][8 * m + 2] * ps, s[u][8 * m + 3] * ps);
+      const uint32_t p1 =
+          pack_fp8x4(s[u][8 * m + 4] * ps, s[u][8 * m + 5] * ps, s[u][8 * m + 6] * ps, s[u][8 * m + 7] * ps);
+      if constexpr (g + 1 < 2 * C::NT) {
+        read_group(int_c<g + 1>{});
+        lgkm_wait<C::TV>();
+      } else {
+        lgkm_wait<0>();
       }
-    }
+      static_for<C::TV>([&](auto T_) {
+        constexpr int t = decltype(T_)::value;
+        tie(vr[g & 1][t]);
+        acc[t] = mfma32_fp8(acc[t], (uint32_t)vr[g & 1][t].x, (uint32_t)vr[g & 1][t].y, p0, p1);
+      });
+    });
 #pragma unroll
     for (int u = 0; u < C::NT; ++u) s_cur[u] = s_nxt[u];
-  };
-
-  for (int it = 0; it < n_iter; it += 2) {
-    body(0, it);
-    if (it + 1 < n_iter) body(1, it + 1);
+    st = st1;
   }
+  // the ring's last loads (empty descriptors) must retire before the
+  // workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);

@@ -115,6 +115,63 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nbytes, 0x00020000);
 }
 
+// ---- LDS transpose reads as inline assembly
+// The compiler's wait-counter pass cannot tell a builtin transpose read from
+// an LDS read that aliases a pending buffer->LDS load, so it puts a full
+// vmcnt(0) in front of the first one: PV would then wait for the loads of the
+// next key blocks.  These kernels order their direct-to-LDS loads themselves
+// (explicit vmcnt waits before each block barrier), so the V^T reads are
+// issued as asm.  The compiler does not count them, so they are completed with
+// lgkm_wait<N>() followed by tie() on every loaded register: tie's "+v"
+// operand makes each consumer come after the wait.  Counting stays correct
+// whatever else the compiler interleaves: LDS operations retire in order, and
+// extra operations only make a count-based wait stricter.
+template <int... I>
+struct int_seq {};
+template <int N, int... I>
+struct make_int_seq : make_int_seq<N - 1, N - 1, I...> {};
+template <int... I>
+struct make_int_seq<0, I...> {
+  using type = int_seq<I...>;
+};
+template <int V>
+struct int_c {
+  static constexpr int value = V;
+};
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, int_seq<I...>) {
+  (f(int_c<I>{}), ...);
+}
+// f(int_c<0>{}), ..., f(int_c<N-1>{}): loop indices usable as constants
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, typename make_int_seq<N>::type{});
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)ptr;
+}
+template <int OFF>
+__device__ __forceinline__ i32x2 lds_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ i32x2 lds_tr8(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+__device__ __forceinline__ void tie(i32x2& r) { asm volatile("" : "+v"(r)); }
+
 template <class C>
 __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
   constexpr int DT = C::DT;
@@ -233,6 +290,9 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
 #pragma unroll
   for (int t = 0; t < C::TV; ++t)
     voff[t] = (4 * hl + e4) * C::ROWB + v_slot<C::ROWB>(e4, 4 * t + 2 * grp + (jq >> 1)) * 16 + 8 * (jq & 1);
+  uint32_t va[C::TV];  // LDS addresses of the V^T reads (stage and row offsets are immediates)
+#pragma unroll
+  for (int t = 0; t < C::TV; ++t) va[t] = lds_addr(smem) + (uint32_t)voff[t];
 
   // zero both stages once so no slot is ever read uninitialised
 #pragma unroll
@@ -282,9 +342,10 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
     qk(s_cur, 0);
   }
 
-  // ST = it % 2, passed as a literal at both call sites so the stage offsets
-  // fold into the LDS instructions' immediate offsets after inlining
-  auto body = [&](const int ST, int it) {
+  // ST = it % 2 as a compile-time constant, so the stage offsets fold into
+  // the LDS instructions' immediate offsets
+  auto body = [&](auto ST_, int it) {
+    constexpr int ST = decltype(ST_)::value;
     const int j0 = j_begin + it * C::BN;
     // loads of K(it+1) and V(it) have landed everywhere, and every wave is done
     // with K stage ST (QK(it)) and V stage ST^1 (PV(it-1))
@@ -295,7 +356,6 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
     // QK of the next block goes to the MFMA pipe while this block's softmax
     // runs on the VALU
     if (it + 1 < n_iter) qk(s_nxt, ST ^ 1);
-    const char* Vs = smem + ST * C::STAGE + C::TILE;
     f32x16 (&s)[C::NT] = s_cur;
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
@@ -337,45 +397,49 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
       }
     }
     l_run += rs;
-    // O^T += V^T P^T, 16 keys per MFMA: tile u, half m covers keys 32u+16m+{0..15}
-#pragma unroll
-    for (int u = 0; u < C::NT; ++u) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        u32x4 pf;
-        pf.x = pack2_p<DT>(s[u][8 * m + 0], s[u][8 * m + 1]);
-        pf.y = pack2_p<DT>(s[u][8 * m + 2], s[u][8 * m + 3]);
-        pf.z = pack2_p<DT>(s[u][8 * m + 4], s[u][8 * m + 5]);
-        pf.w = pack2_p<DT>(s[u][8 * m + 6], s[u][8 * m + 7]);
-        // lane 4e+jq of 16-lane group (hl, grp) reads row 32u+16m+8q+4hl+e,
-        // columns 32t+16grp+4jq..+3; it receives column lr of those 4 rows
-        u32x4 vf[C::TV];
-#pragma unroll
-        for (int t = 0; t < C::TV; ++t) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const char* a = Vs + (32 * u + 16 * m + 8 * q) * C::ROWB + voff[t];
-            const i32x2 x = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a)));
-            if (q == 0) {
-              vf[t].x = (uint32_t)x.x;
-              vf[t].y = (uint32_t)x.y;
-            } else {
-              vf[t].z = (uint32_t)x.x;
-              vf[t].w = (uint32_t)x.y;
-            }
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < C::TV; ++t) acc[t] = mfma32<DT>(acc[t], vf[t], pf);
+    // O^T += V^T P^T, 16 keys per MFMA: group g = (u, m) covers keys
+    // 32u+16m+{0..15}.  Lane 4e+jq of 16-lane group (hl, grp) reads row
+    // 32u+16m+8q+4hl+e, columns 32t+16grp+4jq..+3, and receives column lr of
+    // those 4 rows.  The reads of group g+1 are in flight during group g's MFMAs.
+    i32x2 vr[2][C::TV][2];
+    auto read_group = [&](auto G_) {
+      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
+      static_for<C::TV>([&](auto T_) {
+        constexpr int t = decltype(T_)::value;
+        vr[g & 1][t][0] = lds_tr16<ST * C::STAGE + C::TILE + (32 * u + 16 * m) * C::ROWB>(va[t]);
+        vr[g & 1][t][1] = lds_tr16<ST * C::STAGE + C::TILE + (32 * u + 16 * m + 8) * C::ROWB>(va[t]);
+      });
+    };
+    read_group(int_c<0>{});
+    static_for<2 * C::NT>([&](auto G_) {
+      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
+      u32x4 pf;
+      pf.x = pack2_p<DT>(s[u][8 * m + 0], s[u][8 * m + 1]);
+      pf.y = pack2_p<DT>(s[u][8 * m + 2], s[u][8 * m + 3]);
+      pf.z = pack2_p<DT>(s[u][8 * m + 4], s[u][8 * m + 5]);
+      pf.w = pack2_p<DT>(s[u][8 * m + 6], s[u][8 * m + 7]);
+      if constexpr (g + 1 < 2 * C::NT) {
+        read_group(int_c<g + 1>{});
+        lgkm_wait<2 * C::TV>();
+      } else {
+        lgkm_wait<0>();
       }
-    }
+      static_for<C::TV>([&](auto T_) {
+        constexpr int t = decltype(T_)::value;
+        tie(vr[g & 1][t][0]);
+        tie(vr[g & 1][t][1]);
+        const u32x4 vf = {(uint32_t)vr[g & 1][t][0].x, (uint32_t)vr[g & 1][t][0].y, (uint32_t)vr[g & 1][t][1].x,
+                          (uint32_t)vr[g & 1][t][1].y};
+        acc[t] = mfma32<DT>(acc[t], vf, pf);
+      });
+    });
 #pragma unroll
     for (int u = 0; u < C::NT; ++u) s_cur[u] = s_nxt[u];
   };
 
   for (int it = 0; it < n_iter; it += 2) {
-    body(0, it);
-    if (it + 1 < n_iter) body(1, it + 1);
+    body(int_c<0>{}, it);
+    if (it + 1 < n_iter) body(int_c<1>{}, it + 1);
   }
 
   // ---- epilogue
