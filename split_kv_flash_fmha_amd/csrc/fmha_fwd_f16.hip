@@ -45,13 +45,16 @@ const FwdKernel* registry_f16_decode(int* n) {
   return kDecTable;
 }
 
-// Prefill instances (32x32 MFMA tiles, 4 waves x 32 rows, 64 keys per iteration).
-#define FMHA_PF(D, ID) \
-  {DT_F16, D, D, 4, 1, 64, ID, &launch_prefill<PfCfg<DT_F16, D, 4, 64>>}
+// Prefill instances (32x32 MFMA tiles, 4 waves x 32 rows; key blocks of 32
+// keys for D = 128 and 64 keys for D = 64, 8 KiB of K or V per block).  Two
+// workgroups share a CU, so the two waves on a SIMD belong to different
+// workgroups and drift out of phase (one on MFMA while the other is on VALU).
+#define FMHA_PF(D, NWM, BN, ID) \
+  {DT_F16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, NWM, BN>>}
 
 static const FwdKernel kPfTable[] = {
-    FMHA_PF(64, 200),
-    FMHA_PF(128, 201),
+    FMHA_PF(64, 4, 64, 200),
+    FMHA_PF(128, 4, 32, 201),
 };
 
 const FwdKernel* registry_f16_prefill(int* n) {

@@ -138,6 +138,40 @@ __device__ __forceinline__ u32x4 pack_p(const f32x4* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Work item (split, kv head, sequence, query tile) of this workgroup.
+// Items are ordered so that the query tiles and splits of one (sequence, kv
+// head) -- the workgroups that stream the same K and V -- form one group of
+// consecutive items, query tiles in descending order (in a causal tile the
+// later rows see more keys, so the longest items start first).  Workgroups go
+// to the 8 XCDs round-robin (block i on XCD i % 8) and each XCD has its own L2:
+// groups are dealt to XCDs in rounds of 8, a whole group to one XCD, so the
+// workgroups sharing K and V run on one XCD at about the same time.  A last
+// round of fewer than 8 groups is dealt block by block.
+struct WorkItem {
+  int split, hkv, b, qtile;
+};
+__device__ __forceinline__ WorkItem work_item(const FwdParams& p) {
+  constexpr uint32_t kXcds = 8;
+  const uint32_t bid = blockIdx.x;
+  const uint32_t gsz = (uint32_t)p.num_q_tiles * (uint32_t)p.num_splits;  // items per group
+  const uint32_t ngroups = (uint32_t)p.batch * (uint32_t)p.hkv;
+  const uint32_t round_items = kXcds * gsz;
+  const uint32_t full = (ngroups / kXcds) * round_items;
+  uint32_t item = bid;
+  if (bid < full) {
+    const uint32_t r = bid / round_items, local = bid % round_items;
+    item = (r * kXcds + local % kXcds) * gsz + local / kXcds;
+  }
+  WorkItem w;
+  w.qtile = p.num_q_tiles - 1 - (int)(item % (uint32_t)p.num_q_tiles);
+  item /= (uint32_t)p.num_q_tiles;
+  w.split = (int)(item % (uint32_t)p.num_splits);
+  item /= (uint32_t)p.num_splits;
+  w.hkv = (int)(item % (uint32_t)p.hkv);
+  w.b = (int)(item / (uint32_t)p.hkv);
+  return w;
+}
+
 __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
@@ -211,15 +245,9 @@ __global__ __launch_bounds__(C::NTHR) void fmha_fwd_kernel(FwdParams p) {
 
   // ---- tile decode: split fastest, then kv head, batch, query tile (reversed,
   // so the heaviest tiles of causal / long sequences are dispatched first)
-  int64_t bid = blockIdx.x;
+  const WorkItem wi = work_item(p);
   const int S = p.num_splits;
-  const int split = (int)(bid % S);
-  bid /= S;
-  const int hkv = (int)(bid % p.hkv);
-  bid /= p.hkv;
-  const int b = (int)(bid % p.batch);
-  bid /= p.batch;
-  const int qtile = p.num_q_tiles - 1 - (int)bid;
+  const int split = wi.split, hkv = wi.hkv, b = wi.b, qtile = wi.qtile;
 
   int q_off, sq, k_off, sk;
   if (p.cu_q) {

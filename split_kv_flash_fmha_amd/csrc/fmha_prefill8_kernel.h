@@ -69,15 +69,9 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   const int hl = lane >> 5;
   const int lr = lane & 31;
 
-  int64_t bid = blockIdx.x;
+  const WorkItem wi = work_item(p);
   const int S = p.num_splits;
-  const int split = (int)(bid % S);
-  bid /= S;
-  const int hkv = (int)(bid % p.hkv);
-  bid /= p.hkv;
-  const int b = (int)(bid % p.batch);
-  bid /= p.batch;
-  const int qtile = p.num_q_tiles - 1 - (int)bid;
+  const int split = wi.split, hkv = wi.hkv, b = wi.b, qtile = wi.qtile;
 
   int q_off, sq, k_off, sk;
   if (p.cu_q) {
@@ -224,7 +218,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     issue_k(j_begin + 2 * C::BN, 2);
     issue_v(j_begin + C::BN, 1);
     wait_older_loads();  // K(0), V(0), K(1) landed
-    __syncthreads();
+    block_barrier();
     qk(s_cur, 0);
   }
 
@@ -234,7 +228,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     const int st1 = st == 2 ? 0 : st + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     wait_older_loads();
-    __syncthreads();  // K(it+1), V(it) in LDS everywhere; stages of K(it), V(it-1) free
+    block_barrier();  // K(it+1), V(it) in LDS everywhere; stages of K(it), V(it-1) free
     issue_k(j0 + 3 * C::BN, st);
     issue_v(j0 + 2 * C::BN, st2);
     if (it + 1 < n_iter) qk(s_nxt, st1);

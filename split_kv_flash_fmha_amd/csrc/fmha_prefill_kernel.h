@@ -1,6 +1,6 @@
 // Prefill kernel for gfx950: many query rows per (sequence, kv head), so the
 // work is a dense contraction on MFMA.  One workgroup = NWM waves x 32 query
-// rows; per iteration it stages BN keys of K and V in LDS and every wave runs
+// rows; per key block of BN keys every wave runs
 //   S^T[key, row] = K Q^T       (v_mfma_f32_32x32x16_{f16,bf16}, A = K, B = Q^T)
 //   O^T[dv, row] += V^T P^T     (A = V^T via ds_read_b64_tr_b16, B = P^T)
 // with the online exp2 softmax in between (flash attention forward; web pages
@@ -17,8 +17,14 @@
 // K and V blocks move HBM -> LDS with buffer loads that write LDS directly
 // (16 bytes per lane, no register staging), rows unpadded with an XOR chunk
 // swizzle that keeps both the 16-byte K reads and the V transpose reads free
-// of bank conflicts.  The LDS holds two key blocks: block n+1 is in flight while
-// block n is computed, one barrier per block.
+// of bank conflicts.  K and V each have a ring of three LDS stages; the loads
+// run two blocks ahead of their use, one barrier per block.
+//
+// Software pipeline: iteration n runs PV(n-1) on the MFMA pipe while the VALU
+// takes the row max of block n, then QK(n+1) on the MFMA pipe while the VALU
+// takes the exponentials of block n.  The MFMAs and the VALU work are
+// interleaved in chunks inside each wave, so both pipes stay busy even when
+// the other wave on the SIMD is stalled.
 //
 // Softmax bookkeeping uses a lazily moved reference max per row: p =
 // exp2(scale*s - m_ref) with m_ref moved (and O, l rescaled by
@@ -70,21 +76,23 @@ struct PfCfg {
   static constexpr int DT = DT_;
   static constexpr int D = D_;          // Dqk == Dv
   static constexpr int NWM = NWM_;      // waves, 32 rows each
-  static constexpr int BN = BN_;        // keys per iteration
+  static constexpr int BN = BN_;        // keys per block
   static constexpr int NTHR = 64 * NWM;
   static constexpr int ROWS = 32 * NWM;
   static constexpr int KS = D / 16;     // k-steps of QK (16 d each)
   static constexpr int NT = BN / 32;    // S^T tiles (32 keys each)
   static constexpr int TV = D / 32;     // O^T tiles (32 dv each)
+  static constexpr int NG = 2 * NT;     // PV groups (16 keys each)
   static constexpr int ROWB = D * 2;    // bytes per K / V row (unpadded, swizzled)
   static constexpr int RPL = 1024 / ROWB;          // rows per 1 KiB direct-to-LDS load
-  static constexpr int TILE = BN * ROWB;           // one K or V block
-  static constexpr int LOADS = 2 * TILE / 1024;    // 1 KiB loads per K+V block
-  static constexpr int LPW = LOADS / NWM;          // per wave
-  static constexpr int STAGE = 2 * TILE;
-  static constexpr int LDS = 2 * STAGE;            // double buffered
+  static constexpr int TILE = BN * ROWB;           // one K or V block in LDS
+  static constexpr int KL = TILE / 1024 / NWM;     // 1 KiB loads per wave per K (or V) block
+  static constexpr int NS = 4;                     // ring depth, K and V each
+  static constexpr int LDS = 2 * NS * TILE;
+  static constexpr int MIN_BLOCKS = 8 / NWM;       // two waves per SIMD
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
-  static_assert(1024 % ROWB == 0 && LOADS % (2 * NWM) == 0, "whole 1 KiB K and V loads per wave");
+  static_assert(1024 % ROWB == 0 && KL >= 1 && KL * NWM * 1024 == TILE, "whole 1 KiB loads per wave");
+  static_assert(TILE % 256 == 0, "stage offsets keep the low address bits");
 };
 
 // 16-byte chunk c of row r sits at chunk slot c ^ swz(r) (an XOR on the low
@@ -115,17 +123,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nbytes, 0x00020000);
 }
 
-// ---- LDS transpose reads as inline assembly
-// The compiler's wait-counter pass cannot tell a builtin transpose read from
-// an LDS read that aliases a pending buffer->LDS load, so it puts a full
-// vmcnt(0) in front of the first one: PV would then wait for the loads of the
-// next key blocks.  These kernels order their direct-to-LDS loads themselves
-// (explicit vmcnt waits before each block barrier), so the V^T reads are
+// Workgroup barrier without the memory-model fences of __syncthreads(): its
+// release fence makes the compiler wait for every buffer->LDS load in flight
+// (vmcnt(0)), which would drain the load ring at every key block.  The
+// kernels wait for the loads a block needs themselves (vmcnt with a count)
+// and complete their LDS reads (lgkmcnt) before each barrier; the empty asm
+// statements keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---- LDS reads as inline assembly
+// The compiler's wait-counter pass cannot tell an LDS read from one that
+// aliases a pending buffer->LDS load, so it puts a full vmcnt(0) in front of
+// such reads: the MFMAs would then wait for the loads of the next key blocks.
+// These kernels order their direct-to-LDS loads themselves (explicit vmcnt
+// waits before each block barrier), so the K and V^T fragment reads are
 // issued as asm.  The compiler does not count them, so they are completed with
 // lgkm_wait<N>() followed by tie() on every loaded register: tie's "+v"
 // operand makes each consumer come after the wait.  Counting stays correct
 // whatever else the compiler interleaves: LDS operations retire in order, and
-// extra operations only make a count-based wait stricter.
+// extra operations only make a count-based wait stricter.  tie() on a
+// computed value also pins the computation before that point (volatile asm
+// keeps its order), which stops the compiler from sinking VALU work meant to
+// overlap the MFMAs into the block that consumes it.
 template <int... I>
 struct int_seq {};
 template <int N, int... I>
@@ -170,28 +193,37 @@ __device__ __forceinline__ void lgkm_wait() {
   static_assert(N >= 0 && N < 16, "lgkmcnt");
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
 }
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
 __device__ __forceinline__ void tie(i32x2& r) { asm volatile("" : "+v"(r)); }
+__device__ __forceinline__ void tie(u32x4& r) { asm volatile("" : "+v"(r)); }
+__device__ __forceinline__ void tie(float& r) { asm volatile("" : "+v"(r)); }
+// max over the two 32-lane halves of the wave (lane i and lane i ^ 32)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 template <class C>
-__global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
+__global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(FwdParams p) {
   constexpr int DT = C::DT;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  // 256-byte alignment: stage offsets and the XOR swizzles compose by addition
+  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wm = tid >> 6;
+  const int wm = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int hl = lane >> 5;   // lane half: contraction slots / output row group
   const int lr = lane & 31;   // query row within the wave / MFMA column
 
-  int64_t bid = blockIdx.x;
+  const WorkItem wi = work_item(p);
   const int S = p.num_splits;
-  const int split = (int)(bid % S);
-  bid /= S;
-  const int hkv = (int)(bid % p.hkv);
-  bid /= p.hkv;
-  const int b = (int)(bid % p.batch);
-  bid /= p.batch;
-  const int qtile = p.num_q_tiles - 1 - (int)bid;
+  const int split = wi.split, hkv = wi.hkv, b = wi.b, qtile = wi.qtile;
 
   int q_off, sq, k_off, sk;
   if (p.cu_q) {
@@ -260,103 +292,187 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // One key block = LOADS buffer->LDS loads of 1 KiB (RPL rows each): wave wm
-  // issues loads [wm*LPW, (wm+1)*LPW), K loads first, then V.  Lane l of a
-  // load writes LDS bytes [16l, 16l+16) of it, i.e. slot l % (ROWB/16) of row
-  // l / (ROWB/16), so it fetches the chunk that belongs in that slot.  Its
-  // byte offset from the block's first row is a loop constant; the block base
-  // goes into the buffer descriptor, whose size ends at the last valid key, so
-  // rows past the key range read as zero.
+  // One K (or V) block = NWM * KL buffer->LDS loads of 1 KiB (RPL rows each);
+  // wave wm issues loads [wm*KL, (wm+1)*KL).  Lane l of a load writes LDS
+  // bytes [16l, 16l+16) of it, i.e. slot l % (ROWB/16) of row l / (ROWB/16),
+  // so it fetches the chunk that belongs in that slot.  Its byte offset from
+  // the block's first row is a loop constant; the block base goes into the
+  // buffer descriptor, whose size ends at the last row the tile needs, so rows
+  // past it read as zero, and a block past it gets an empty descriptor
+  // (nothing is fetched).  Every wave issues the same number of loads per
+  // block, so the loads in flight are a compile-time count.
   constexpr int CPR = C::ROWB / 16;  // chunks per row
-  // wave wm loads rows [wm * LPW/2 * RPL, ...) of the K tile and of the V tile
-  int kld_off[C::LPW / 2], vld_off[C::LPW / 2];
+  int kld_off[C::KL], vld_off[C::KL];
 #pragma unroll
-  for (int n = 0; n < C::LPW / 2; ++n) {
-    const int lrow = (wm * C::LPW / 2 + n) * C::RPL + lane / CPR;
+  for (int n = 0; n < C::KL; ++n) {
+    const int lrow = (wm * C::KL + n) * C::RPL + lane / CPR;
     kld_off[n] = lrow * (int)p.k_st + k_slot<C::ROWB>(lrow, lane % CPR) * 16;
     vld_off[n] = lrow * (int)p.v_st + v_slot<C::ROWB>(lrow, lane % CPR) * 16;
   }
-  // LDS read offsets (bytes within a stage's K / V tile), loop constants
-  int koff[C::NT][C::KS];
+  const uint32_t lds0 = lds_addr(smem);
+  // K fragment read addresses: k-step k of tile u (row 32u + lr) sits at
+  // (kaddr[u] ^ 32k) within a stage (the swizzle only touches bits 5..7); the
+  // stage offset is an immediate
+  static_assert(C::ROWB == 256 || C::ROWB == 128, "swizzles");
+  uint32_t kx[C::NT][C::KS];
 #pragma unroll
-  for (int u = 0; u < C::NT; ++u)
+  for (int u = 0; u < C::NT; ++u) {
+    const int kaddr = (32 * u + lr) * C::ROWB + k_slot<C::ROWB>(32 * u + lr, hl) * 16;
 #pragma unroll
-    for (int k = 0; k < C::KS; ++k) {
-      const int row = 32 * u + lr;
-      koff[u][k] = row * C::ROWB + k_slot<C::ROWB>(row, 2 * k + hl) * 16;
-    }
+    for (int k = 0; k < C::KS; ++k) kx[u][k] = lds0 + (uint32_t)(kaddr ^ (32 * k));
+  }
+  // V^T read address of this lane for O^T tile t (dv 32t..) within a stage is
+  // vaddr ^ 64t; stage and row steps are immediates
   const int e4 = (lane >> 2) & 3, jq = lane & 3, grp = (lane >> 4) & 1;
-  int voff[C::TV];  // + (32u + 16m + 8q) * ROWB per read (row & 3 == e4 throughout)
+  const int vaddr = (4 * hl + e4) * C::ROWB + v_slot<C::ROWB>(e4, 2 * grp + (jq >> 1)) * 16 + 8 * (jq & 1);
+  uint32_t vx[C::TV];
 #pragma unroll
-  for (int t = 0; t < C::TV; ++t)
-    voff[t] = (4 * hl + e4) * C::ROWB + v_slot<C::ROWB>(e4, 4 * t + 2 * grp + (jq >> 1)) * 16 + 8 * (jq & 1);
-  uint32_t va[C::TV];  // LDS addresses of the V^T reads (stage and row offsets are immediates)
-#pragma unroll
-  for (int t = 0; t < C::TV; ++t) va[t] = lds_addr(smem) + (uint32_t)voff[t];
+  for (int t = 0; t < C::TV; ++t) vx[t] = lds0 + (uint32_t)(C::NS * C::TILE + (vaddr ^ (64 * t)));
 
-  // zero both stages once so no slot is ever read uninitialised
+  // zero the LDS once so no slot is ever read uninitialised
 #pragma unroll
   for (int i = tid * 16; i < C::LDS; i += C::NTHR * 16) *(u32x4*)(smem + i) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  // K and V of block b live in K stage b%2 / V stage b%2.  K runs one block
-  // ahead of V: during iteration it the loads of K(it+2) and V(it+1) are in
-  // flight while QK(it+1) and PV(it) are computed.
-  auto issue_k = [&](int j0, int stage) {
-    const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc(kbase + (int64_t)j0 * p.k_st, (int64_t)min(ke - 1 - j0, C::BN) * p.k_st + C::ROWB);
-    char* base = smem + stage * C::STAGE;
-#pragma unroll
-    for (int n = 0; n < C::LPW / 2; ++n) buffer_to_lds16(rk, base + (wm * C::LPW / 2 + n) * 1024, kld_off[n]);
+  // descriptor of key block jb: rows [jb, min(jb + BN, j_end)) of K or V
+  auto block_rsrc = [&](const char* base, int64_t st, int jb) {
+    const int rows_left = min(j_end - jb, C::BN);
+    const int nb = rows_left > 0 ? (rows_left - 1) * (int)st + C::ROWB : 0;
+    return make_rsrc(base + (int64_t)jb * st, nb);
   };
-  auto issue_v = [&](int j0, int stage) {
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(vbase + (int64_t)j0 * p.v_st, (int64_t)min(ke - 1 - j0, C::BN) * p.v_st + C::ROWB);
-    char* base = smem + stage * C::STAGE + C::TILE;
+  auto issue_k = [&](int jb, auto ST_) {
+    constexpr int ST = decltype(ST_)::value;
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, p.k_st, jb);
 #pragma unroll
-    for (int n = 0; n < C::LPW / 2; ++n) buffer_to_lds16(rv, base + (wm * C::LPW / 2 + n) * 1024, vld_off[n]);
+    for (int n = 0; n < C::KL; ++n) buffer_to_lds16(rk, smem + ST * C::TILE + (wm * C::KL + n) * 1024, kld_off[n]);
   };
-  auto qk = [&](f32x16 (&sd)[C::NT], int stage) {
-    const char* Ks = smem + stage * C::STAGE;
+  auto issue_v = [&](int jb, auto ST_) {
+    constexpr int ST = decltype(ST_)::value;
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, p.v_st, jb);
 #pragma unroll
-    for (int u = 0; u < C::NT; ++u)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sd[u][e] = 0.f;
-#pragma unroll
-    for (int k = 0; k < C::KS; ++k) {
-      u32x4 kf[C::NT];
-#pragma unroll
-      for (int u = 0; u < C::NT; ++u) kf[u] = *(const u32x4*)(Ks + koff[u][k]);
-#pragma unroll
-      for (int u = 0; u < C::NT; ++u) sd[u] = mfma32<DT>(sd[u], kf[u], qf[k]);
-    }
+    for (int n = 0; n < C::KL; ++n)
+      buffer_to_lds16(rv, smem + (C::NS + ST) * C::TILE + (wm * C::KL + n) * 1024, vld_off[n]);
+  };
+  // at most `n` of this wave's loads in flight (they retire in order)
+  auto wait_loads = [](auto N_) {
+    constexpr int n = decltype(N_)::value;
+    static_assert(n < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
   };
 
-  f32x16 s_cur[C::NT], s_nxt[C::NT];
+  // P of the previous block, packed for the PV MFMA (group g: keys 16g..16g+15)
+  u32x4 pprev[C::NG];
+
+  // O^T += V^T P^T for one key block from V stage VST.  Lane 4e+jq of 16-lane
+  // group (hl, grp) reads row 16g+8q+4hl+e, columns 32t+16grp+4jq..+3, and
+  // receives column lr of those 4 rows.  MFMA n = (group g, tile t) takes its
+  // V^T fragment from slot n % 3 of a ring filled two MFMAs ahead;
+  // `between(g)` is VALU work placed after group g.
+  auto pv = [&](auto VST_, auto&& between) {
+    constexpr int VST = decltype(VST_)::value;
+    constexpr int NM = C::NG * C::TV;
+    i32x2 vr[3][2];
+    auto read_frag = [&](auto N_) {
+      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
+      vr[n % 3][0] = lds_tr16<VST * C::TILE + (16 * g) * C::ROWB>(vx[t]);
+      vr[n % 3][1] = lds_tr16<VST * C::TILE + (16 * g + 8) * C::ROWB>(vx[t]);
+    };
+    read_frag(int_c<0>{});
+    if constexpr (NM > 1) read_frag(int_c<1>{});
+    static_for<NM>([&](auto N_) {
+      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
+      if constexpr (n + 2 < NM) {
+        read_frag(int_c<n + 2>{});
+        lgkm_wait<4>();  // fragments n+1 and n+2 may still be in flight
+      } else if constexpr (n + 1 < NM) {
+        lgkm_wait<2>();
+      } else {
+        lgkm_wait<0>();
+      }
+      tie(vr[n % 3][0]);
+      tie(vr[n % 3][1]);
+      const u32x4 vf = {(uint32_t)vr[n % 3][0].x, (uint32_t)vr[n % 3][0].y, (uint32_t)vr[n % 3][1].x,
+                        (uint32_t)vr[n % 3][1].y};
+      acc[t] = mfma32<DT>(acc[t], vf, pprev[g]);
+      if constexpr (t + 1 == C::TV) between(int_c<g>{});
+    });
+  };
+
+  // S^T = K Q^T for one key block from K stage KST into sd, tile-major, one
+  // MFMA per chunk; MFMA n takes its K fragment from slot n % 3 of a ring
+  // filled two MFMAs ahead; `between(n)` is VALU work placed after MFMA n.
+  auto qk = [&](auto KST_, f32x16 (&sd)[C::NT], auto&& between) {
+    constexpr int KST = decltype(KST_)::value;
+    constexpr int NM = C::NT * C::KS;
+    u32x4 kf[3];
+    auto read_k = [&](auto N_) {
+      constexpr int n = decltype(N_)::value, u = n / C::KS, k = n % C::KS;
+      kf[n % 3] = lds_b128<KST * C::TILE>(kx[u][k]);
+    };
+    read_k(int_c<0>{});
+    if constexpr (NM > 1) read_k(int_c<1>{});
+    static_for<NM>([&](auto N_) {
+      constexpr int n = decltype(N_)::value, u = n / C::KS, k = n % C::KS;
+      if constexpr (n + 2 < NM) {
+        read_k(int_c<n + 2>{});
+        lgkm_wait<2>();
+      } else if constexpr (n + 1 < NM) {
+        lgkm_wait<1>();
+      } else {
+        lgkm_wait<0>();
+      }
+      tie(kf[n % 3]);
+      if constexpr (k == 0) {
+        f32x16 z;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = 0.f;
+        sd[u] = mfma32<DT>(z, kf[n % 3], qf[k]);
+      } else {
+        sd[u] = mfma32<DT>(sd[u], kf[n % 3], qf[k]);
+      }
+      between(int_c<n>{});
+    });
+  };
+  auto nothing = [](auto) {};
+
+  // Ring of NS = 4 stages for K and for V: K(b) in K stage b%4, V(b) in V
+  // stage b%4.  Iteration it issues K(it+4) and V(it+2) and needs K(it+1)
+  // (QK) and V(it-1) (PV), both issued three iterations back: the loads of
+  // the two previous iterations may stay in flight.  The prologue issues in
+  // the same order as iterations -4..-1 would (with empty loads for V(-2) and
+  // V(-1)), so the count is uniform.
+  static_assert(C::NS == 4, "ring schedule");
+  f32x16 sbuf[2][C::NT];  // S of block it in sbuf[it % 2]
+  const int jlast = j_begin + n_iter * C::BN;  // first block past the tile's range
   if (n_iter > 0) {
-    issue_k(j_begin, 0);
-    issue_v(j_begin, 0);
-    if (n_iter > 1) issue_k(j_begin + C::BN, 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    qk(s_cur, 0);
+    issue_k(j_begin, int_c<0>{});
+    issue_v(jlast, int_c<2>{});  // empty
+    issue_k(j_begin + C::BN, int_c<1>{});
+    issue_v(jlast, int_c<3>{});  // empty
+    issue_k(j_begin + 2 * C::BN, int_c<2>{});
+    issue_v(j_begin, int_c<0>{});
+    issue_k(j_begin + 3 * C::BN, int_c<3>{});
+    issue_v(j_begin + C::BN, int_c<1>{});
+    wait_loads(int_c<7 * C::KL>{});  // K(0) landed
+    block_barrier();
+    qk(int_c<0>{}, sbuf[0], nothing);
   }
 
-  // ST = it % 2 as a compile-time constant, so the stage offsets fold into
-  // the LDS instructions' immediate offsets
-  auto body = [&](auto ST_, int it) {
+  // ST = it % 4 at compile time: every LDS stage offset is an immediate.
+  // FIRST: it == 0 (no PV of a previous block).  The last iteration also runs
+  // QK of the block after the tile (an empty, zero-filled stage) and drops it.
+  auto body = [&](auto ST_, auto FIRST_, int it) {
     constexpr int ST = decltype(ST_)::value;
+    constexpr int SB = ST & 1;
+    constexpr bool FIRST = decltype(FIRST_)::value != 0;
     const int j0 = j_begin + it * C::BN;
-    // loads of K(it+1) and V(it) have landed everywhere, and every wave is done
-    // with K stage ST (QK(it)) and V stage ST^1 (PV(it-1))
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 2 < n_iter) issue_k(j0 + 2 * C::BN, ST);
-    if (it + 1 < n_iter) issue_v(j0 + C::BN, ST ^ 1);
-    // QK of the next block goes to the MFMA pipe while this block's softmax
-    // runs on the VALU
-    if (it + 1 < n_iter) qk(s_nxt, ST ^ 1);
-    f32x16 (&s)[C::NT] = s_cur;
+    // K(it+1), V(it-1) landed everywhere; every wave is done with K stage ST
+    // (QK(it)) and V stage (it+2)%4 (PV(it-2))
+    wait_loads(int_c<4 * C::KL>{});
+    block_barrier();
+    issue_k(j0 + 4 * C::BN, int_c<ST>{});
+    issue_v(j0 + 2 * C::BN, int_c<(ST + 2) % 4>{});
+    f32x16 (&s)[C::NT] = sbuf[SB];
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
     if (!full) {
@@ -368,13 +484,22 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
           if (j < my_lo || j > my_hi) s[u][e] = -INFINITY;
         }
     }
-    // raw row max (scale > 0 commutes with max), one exchange with lane ^ 32
+    // PV(it-1) on the MFMA pipe while the raw row max of block it is taken
+    // (scale > 0 commutes with max), a share after each PV group
+    constexpr int MPG = 16 * C::NT / C::NG;
     float mx = -INFINITY;
+    auto max_part = [&](auto G_) {
+      constexpr int g = decltype(G_)::value;
 #pragma unroll
-    for (int u = 0; u < C::NT; ++u)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int i = g * MPG; i < (g + 1) * MPG; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+      tie(mx);
+    };
+    if constexpr (!FIRST) {
+      pv(int_c<(ST + 3) % 4>{}, max_part);
+    } else {
+      static_for<C::NG>([&](auto G_) { max_part(G_); });
+    }
+    mx = max_halves(mx);
     const float m_blk = mx * scale_log2;
     // move the reference max only when some row ran ahead of it by > slack
     if (__any(m_blk > m_run + kRescaleSlack)) {
@@ -385,61 +510,60 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill_kernel(FwdParams p) {
       for (int t = 0; t < C::TV; ++t) acc[t] *= alpha;
       m_run = m_new;
     }
+    // QK(it+1) on the MFMA pipe while the exponentials of block it are taken,
+    // a share after each QK MFMA; P is packed for PV(it) group by group
     const float nbase = -(m_run == -INFINITY ? 0.f : m_run);
+    constexpr int NQ = C::NT * C::KS;
+    constexpr int EPK = 16 * C::NT / NQ;  // exponentials per QK MFMA
+    static_assert(EPK >= 1 && 8 % EPK == 0 && EPK * NQ == 16 * C::NT, "exp chunks vs P groups");
     float rs = 0.f;
+    auto exp_part = [&](auto K_) {
+      constexpr int k = decltype(K_)::value;
 #pragma unroll
-    for (int u = 0; u < C::NT; ++u) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(__builtin_fmaf(s[u][e], scale_log2, nbase));
-        s[u][e] = pe;
+      for (int i = k * EPK; i < (k + 1) * EPK; ++i) {
+        float pe = fast_exp2(__builtin_fmaf(s[i >> 4][i & 15], scale_log2, nbase));
         rs += pe;
+        tie(pe);
+        s[i >> 4][i & 15] = pe;
       }
-    }
-    l_run += rs;
-    // O^T += V^T P^T, 16 keys per MFMA: group g = (u, m) covers keys
-    // 32u+16m+{0..15}.  Lane 4e+jq of 16-lane group (hl, grp) reads row
-    // 32u+16m+8q+4hl+e, columns 32t+16grp+4jq..+3, and receives column lr of
-    // those 4 rows.  The reads of group g+1 are in flight during group g's MFMAs.
-    i32x2 vr[2][C::TV][2];
-    auto read_group = [&](auto G_) {
-      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
-      static_for<C::TV>([&](auto T_) {
-        constexpr int t = decltype(T_)::value;
-        vr[g & 1][t][0] = lds_tr16<ST * C::STAGE + C::TILE + (32 * u + 16 * m) * C::ROWB>(va[t]);
-        vr[g & 1][t][1] = lds_tr16<ST * C::STAGE + C::TILE + (32 * u + 16 * m + 8) * C::ROWB>(va[t]);
-      });
-    };
-    read_group(int_c<0>{});
-    static_for<2 * C::NT>([&](auto G_) {
-      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
-      u32x4 pf;
-      pf.x = pack2_p<DT>(s[u][8 * m + 0], s[u][8 * m + 1]);
-      pf.y = pack2_p<DT>(s[u][8 * m + 2], s[u][8 * m + 3]);
-      pf.z = pack2_p<DT>(s[u][8 * m + 4], s[u][8 * m + 5]);
-      pf.w = pack2_p<DT>(s[u][8 * m + 6], s[u][8 * m + 7]);
-      if constexpr (g + 1 < 2 * C::NT) {
-        read_group(int_c<g + 1>{});
-        lgkm_wait<2 * C::TV>();
-      } else {
-        lgkm_wait<0>();
-      }
-      static_for<C::TV>([&](auto T_) {
-        constexpr int t = decltype(T_)::value;
-        tie(vr[g & 1][t][0]);
-        tie(vr[g & 1][t][1]);
-        const u32x4 vf = {(uint32_t)vr[g & 1][t][0].x, (uint32_t)vr[g & 1][t][0].y, (uint32_t)vr[g & 1][t][1].x,
-                          (uint32_t)vr[g & 1][t][1].y};
-        acc[t] = mfma32<DT>(acc[t], vf, pf);
-      });
-    });
+      tie(rs);
 #pragma unroll
-    for (int u = 0; u < C::NT; ++u) s_cur[u] = s_nxt[u];
+      for (int g = (k * EPK) / 8; g < ((k + 1) * EPK) / 8; ++g) {
+        const int u = g >> 1, m = g & 1;
+        pprev[g].x = pack2_p<DT>(s[u][8 * m + 0], s[u][8 * m + 1]);
+        pprev[g].y = pack2_p<DT>(s[u][8 * m + 2], s[u][8 * m + 3]);
+        pprev[g].z = pack2_p<DT>(s[u][8 * m + 4], s[u][8 * m + 5]);
+        pprev[g].w = pack2_p<DT>(s[u][8 * m + 6], s[u][8 * m + 7]);
+        tie(pprev[g]);
+      }
+    };
+    qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], exp_part);
+    l_run += rs;
   };
 
-  for (int it = 0; it < n_iter; it += 2) {
-    body(int_c<0>{}, it);
-    if (it + 1 < n_iter) body(int_c<1>{}, it + 1);
+  if (n_iter > 0) {
+    body(int_c<0>{}, int_c<1>{}, 0);
+    int it = 1;
+    for (;;) {
+      if (it >= n_iter) break;
+      body(int_c<1>{}, int_c<0>{}, it++);
+      if (it >= n_iter) break;
+      body(int_c<2>{}, int_c<0>{}, it++);
+      if (it >= n_iter) break;
+      body(int_c<3>{}, int_c<0>{}, it++);
+      if (it >= n_iter) break;
+      body(int_c<0>{}, int_c<0>{}, it++);
+    }
+    // PV of the last block (V stage (n_iter-1)%4); every load of the ring
+    // retires here
+    __builtin_amdgcn_s_waitcnt(0);
+    block_barrier();
+    switch ((n_iter - 1) & 3) {
+      case 0: pv(int_c<0>{}, nothing); break;
+      case 1: pv(int_c<1>{}, nothing); break;
+      case 2: pv(int_c<2>{}, nothing); break;
+      default: pv(int_c<3>{}, nothing); break;
+    }
   }
 
   // ---- epilogue
