@@ -203,6 +203,7 @@ __device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
 __device__ __forceinline__ void tie(i32x2& r) { asm volatile("" : "+v"(r)); }
 __device__ __forceinline__ void tie(u32x4& r) { asm volatile("" : "+v"(r)); }
 __device__ __forceinline__ void tie(float& r) { asm volatile("" : "+v"(r)); }
+__device__ __forceinline__ void tie(uint32_t& r) { asm volatile("" : "+v"(r)); }
 // max over the two 32-lane halves of the wave (lane i and lane i ^ 32)
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -360,75 +361,66 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
   };
 
-  // P of the previous block, packed for the PV MFMA (group g: keys 16g..16g+15)
-  u32x4 pprev[C::NG];
+  // P of a key block, packed for the PV MFMA (group g: keys 16g..16g+15):
+  // pbuf[it % 2] holds P(it), so P(it) is produced while PV(it-1) still reads
+  // P(it-1)
+  u32x4 pbuf[2][C::NG];
 
-  // O^T += V^T P^T for one key block from V stage VST.  Lane 4e+jq of 16-lane
-  // group (hl, grp) reads row 16g+8q+4hl+e, columns 32t+16grp+4jq..+3, and
-  // receives column lr of those 4 rows.  MFMA n = (group g, tile t) takes its
-  // V^T fragment from slot n % 3 of a ring filled two MFMAs ahead;
-  // `between(g)` is VALU work placed after group g.
-  auto pv = [&](auto VST_, auto&& between) {
+  // O^T += V^T P^T for one key block from V stage VST with P from pb.  Lane
+  // 4e+jq of 16-lane group (hl, grp) reads row 16g+8q+4hl+e, columns
+  // 32t+16grp+4jq..+3, and receives column lr of those 4 rows.  All fragments
+  // of the block are read up front (two reads per MFMA n = (group g, tile t)),
+  // and MFMA n waits only for its own two; `between(n)` is VALU work placed
+  // after MFMA n.
+  auto pv = [&](auto VST_, const u32x4 (&pb)[C::NG], auto&& between) {
     constexpr int VST = decltype(VST_)::value;
     constexpr int NM = C::NG * C::TV;
-    i32x2 vr[3][2];
-    auto read_frag = [&](auto N_) {
-      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
-      vr[n % 3][0] = lds_tr16<VST * C::TILE + (16 * g) * C::ROWB>(vx[t]);
-      vr[n % 3][1] = lds_tr16<VST * C::TILE + (16 * g + 8) * C::ROWB>(vx[t]);
-    };
-    read_frag(int_c<0>{});
-    if constexpr (NM > 1) read_frag(int_c<1>{});
+    static_assert(2 * NM - 2 <= 15, "lgkmcnt range");
+    i32x2 vr[NM][2];
     static_for<NM>([&](auto N_) {
       constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
-      if constexpr (n + 2 < NM) {
-        read_frag(int_c<n + 2>{});
-        lgkm_wait<4>();  // fragments n+1 and n+2 may still be in flight
-      } else if constexpr (n + 1 < NM) {
-        lgkm_wait<2>();
-      } else {
-        lgkm_wait<0>();
-      }
-      tie(vr[n % 3][0]);
-      tie(vr[n % 3][1]);
-      const u32x4 vf = {(uint32_t)vr[n % 3][0].x, (uint32_t)vr[n % 3][0].y, (uint32_t)vr[n % 3][1].x,
-                        (uint32_t)vr[n % 3][1].y};
-      acc[t] = mfma32<DT>(acc[t], vf, pprev[g]);
-      if constexpr (t + 1 == C::TV) between(int_c<g>{});
+      vr[n][0] = lds_tr16<VST * C::TILE + (16 * g) * C::ROWB>(vx[t]);
+      vr[n][1] = lds_tr16<VST * C::TILE + (16 * g + 8) * C::ROWB>(vx[t]);
+    });
+    static_for<NM>([&](auto N_) {
+      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
+      lgkm_wait<2 * (NM - 1 - n)>();
+      tie(vr[n][0]);
+      tie(vr[n][1]);
+      const u32x4 vf = {(uint32_t)vr[n][0].x, (uint32_t)vr[n][0].y, (uint32_t)vr[n][1].x, (uint32_t)vr[n][1].y};
+      acc[t] = mfma32<DT>(acc[t], vf, pb[g]);
+      between(int_c<n>{});
     });
   };
 
   // S^T = K Q^T for one key block from K stage KST into sd, tile-major, one
-  // MFMA per chunk; MFMA n takes its K fragment from slot n % 3 of a ring
-  // filled two MFMAs ahead; `between(n)` is VALU work placed after MFMA n.
+  // MFMA per chunk; MFMA n takes its K fragment from slot n % KR of a ring
+  // filled KR - 1 MFMAs ahead; `between(n)` is VALU work placed after MFMA n.
   auto qk = [&](auto KST_, f32x16 (&sd)[C::NT], auto&& between) {
     constexpr int KST = decltype(KST_)::value;
     constexpr int NM = C::NT * C::KS;
-    u32x4 kf[3];
+    constexpr int KR = 5;
+    u32x4 kf[KR];
     auto read_k = [&](auto N_) {
       constexpr int n = decltype(N_)::value, u = n / C::KS, k = n % C::KS;
-      kf[n % 3] = lds_b128<KST * C::TILE>(kx[u][k]);
+      kf[n % KR] = lds_b128<KST * C::TILE>(kx[u][k]);
     };
-    read_k(int_c<0>{});
-    if constexpr (NM > 1) read_k(int_c<1>{});
+    static_for<KR - 1>([&](auto N_) {
+      if constexpr (decltype(N_)::value < NM) read_k(N_);
+    });
     static_for<NM>([&](auto N_) {
       constexpr int n = decltype(N_)::value, u = n / C::KS, k = n % C::KS;
-      if constexpr (n + 2 < NM) {
-        read_k(int_c<n + 2>{});
-        lgkm_wait<2>();
-      } else if constexpr (n + 1 < NM) {
-        lgkm_wait<1>();
-      } else {
-        lgkm_wait<0>();
-      }
-      tie(kf[n % 3]);
+      if constexpr (n + KR - 1 < NM) read_k(int_c<n + KR - 1>{});
+      // reads issued after fragment n: min(KR - 1, NM - 1 - n)
+      lgkm_wait<(NM - 1 - n < KR - 1 ? NM - 1 - n : KR - 1)>();
+      tie(kf[n % KR]);
       if constexpr (k == 0) {
         f32x16 z;
 #pragma unroll
         for (int e = 0; e < 16; ++e) z[e] = 0.f;
-        sd[u] = mfma32<DT>(z, kf[n % 3], qf[k]);
+        sd[u] = mfma32<DT>(z, kf[n % KR], qf[k]);
       } else {
-        sd[u] = mfma32<DT>(sd[u], kf[n % 3], qf[k]);
+        sd[u] = mfma32<DT>(sd[u], kf[n % KR], qf[k]);
       }
       between(int_c<n>{});
     });
@@ -458,9 +450,33 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
     qk(int_c<0>{}, sbuf[0], nothing);
   }
 
+  // Softmax with a lazily moved reference: the first block sets each row's
+  // reference m_run from its max; later blocks take p = exp2(scale*s - m_run)
+  // without a max and check afterwards, from the row sums, that no p exceeded
+  // 2^kSumLog2 (every p <= the sum) and that no row with keys in the block is
+  // still without a reference.  Only then (rare) is the row max taken, O and l
+  // rescaled, and the block's exponentials recomputed.  The row sum adds the
+  // fp32 p (the LSE needs them unrounded).
+  constexpr float kSumLimit = 4096.0f;  // 2^12: P stays far inside fp16 range
+  constexpr int NPV = C::NG * C::TV, NQK = C::NT * C::KS;  // MFMAs per phase
+  constexpr int NWD = 8 * C::NT;                           // packed P words per block
+  auto exp_word = [&](const f32x16 (&sd)[C::NT], u32x4 (&pb)[C::NG], float nb, float& rs, auto W_) {
+    constexpr int w = decltype(W_)::value, i = 2 * w;  // elements i, i + 1
+    float p0 = fast_exp2(__builtin_fmaf(sd[i >> 4][i & 15], scale_log2, nb));
+    float p1 = fast_exp2(__builtin_fmaf(sd[(i + 1) >> 4][(i + 1) & 15], scale_log2, nb));
+    uint32_t word = pack2_p<DT>(p0, p1);
+    tie(word);
+    pb[w >> 2][w & 3] = word;
+    rs += p0 + p1;
+    tie(rs);
+  };
+  // words of P done after VALU slot k of NPV + NQK slots (spread evenly)
+  auto words_upto = [](int k) { return (k * NWD) / (NPV + NQK); };
+
   // ST = it % 4 at compile time: every LDS stage offset is an immediate.
-  // FIRST: it == 0 (no PV of a previous block).  The last iteration also runs
-  // QK of the block after the tile (an empty, zero-filled stage) and drops it.
+  // FIRST: it == 0 (no PV of a previous block; the reference is set from the
+  // block max).  The last iteration also runs QK of the block after the tile
+  // (an empty, zero-filled stage) and drops it.
   auto body = [&](auto ST_, auto FIRST_, int it) {
     constexpr int ST = decltype(ST_)::value;
     constexpr int SB = ST & 1;
@@ -473,6 +489,7 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
     issue_k(j0 + 4 * C::BN, int_c<ST>{});
     issue_v(j0 + 2 * C::BN, int_c<(ST + 2) % 4>{});
     f32x16 (&s)[C::NT] = sbuf[SB];
+    u32x4 (&pc)[C::NG] = pbuf[SB];
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
     if (!full) {
@@ -484,60 +501,44 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
           if (j < my_lo || j > my_hi) s[u][e] = -INFINITY;
         }
     }
-    // PV(it-1) on the MFMA pipe while the raw row max of block it is taken
-    // (scale > 0 commutes with max), a share after each PV group
-    constexpr int MPG = 16 * C::NT / C::NG;
-    float mx = -INFINITY;
-    auto max_part = [&](auto G_) {
-      constexpr int g = decltype(G_)::value;
+    auto row_max = [&]() {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = g * MPG; i < (g + 1) * MPG; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
-      tie(mx);
+      for (int u = 0; u < C::NT; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+      return max_halves(mx) * scale_log2;  // scale > 0 commutes with max
+    };
+    if constexpr (FIRST) m_run = row_max();
+    const float nbase = -(m_run == -INFINITY ? 0.f : m_run);
+    float rs = 0.f;
+    // the exponentials of block it are spread over the VALU slots after the
+    // MFMAs of PV(it-1) and QK(it+1)
+    auto slot = [&](auto K_) {
+      constexpr int k = decltype(K_)::value;
+      static_for<words_upto(k + 1) - words_upto(k)>([&](auto W_) {
+        exp_word(s, pc, nbase, rs, int_c<words_upto(k) + decltype(W_)::value>{});
+      });
     };
     if constexpr (!FIRST) {
-      pv(int_c<(ST + 3) % 4>{}, max_part);
+      pv(int_c<(ST + 3) % 4>{}, pbuf[SB ^ 1], [&](auto N_) { slot(N_); });
     } else {
-      static_for<C::NG>([&](auto G_) { max_part(G_); });
+      static_for<NPV>([&](auto N_) { slot(N_); });
     }
-    mx = max_halves(mx);
-    const float m_blk = mx * scale_log2;
-    // move the reference max only when some row ran ahead of it by > slack
-    if (__any(m_blk > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, m_blk);
+    qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(int_c<NPV + decltype(N_)::value>{}); });
+    // reference check (see above); has_keys: the row sees a key of this block
+    const bool has_keys = my_lo <= j0 + C::BN - 1 && my_hi >= j0 && my_lo <= my_hi;
+    if (__any(rs > kSumLimit || (m_run == -INFINITY && has_keys))) {
+      const float m_new = fmaxf(m_run, row_max());
       const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < C::TV; ++t) acc[t] *= alpha;
       m_run = m_new;
+      const float nb2 = -(m_run == -INFINITY ? 0.f : m_run);
+      rs = 0.f;
+      static_for<NWD>([&](auto W_) { exp_word(s, pc, nb2, rs, W_); });
     }
-    // QK(it+1) on the MFMA pipe while the exponentials of block it are taken,
-    // a share after each QK MFMA; P is packed for PV(it) group by group
-    const float nbase = -(m_run == -INFINITY ? 0.f : m_run);
-    constexpr int NQ = C::NT * C::KS;
-    constexpr int EPK = 16 * C::NT / NQ;  // exponentials per QK MFMA
-    static_assert(EPK >= 1 && 8 % EPK == 0 && EPK * NQ == 16 * C::NT, "exp chunks vs P groups");
-    float rs = 0.f;
-    auto exp_part = [&](auto K_) {
-      constexpr int k = decltype(K_)::value;
-#pragma unroll
-      for (int i = k * EPK; i < (k + 1) * EPK; ++i) {
-        float pe = fast_exp2(__builtin_fmaf(s[i >> 4][i & 15], scale_log2, nbase));
-        rs += pe;
-        tie(pe);
-        s[i >> 4][i & 15] = pe;
-      }
-      tie(rs);
-#pragma unroll
-      for (int g = (k * EPK) / 8; g < ((k + 1) * EPK) / 8; ++g) {
-        const int u = g >> 1, m = g & 1;
-        pprev[g].x = pack2_p<DT>(s[u][8 * m + 0], s[u][8 * m + 1]);
-        pprev[g].y = pack2_p<DT>(s[u][8 * m + 2], s[u][8 * m + 3]);
-        pprev[g].z = pack2_p<DT>(s[u][8 * m + 4], s[u][8 * m + 5]);
-        pprev[g].w = pack2_p<DT>(s[u][8 * m + 6], s[u][8 * m + 7]);
-        tie(pprev[g]);
-      }
-    };
-    qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], exp_part);
     l_run += rs;
   };
 
@@ -554,15 +555,16 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
       if (it >= n_iter) break;
       body(int_c<0>{}, int_c<0>{}, it++);
     }
-    // PV of the last block (V stage (n_iter-1)%4); every load of the ring
-    // retires here
+    // PV of the last block (V stage and P buffer of block n_iter-1); every
+    // load of the ring retires here
     __builtin_amdgcn_s_waitcnt(0);
     block_barrier();
-    switch ((n_iter - 1) & 3) {
-      case 0: pv(int_c<0>{}, nothing); break;
-      case 1: pv(int_c<1>{}, nothing); break;
-      case 2: pv(int_c<2>{}, nothing); break;
-      default: pv(int_c<3>{}, nothing); break;
+    const int last = n_iter - 1;
+    switch (last & 3) {
+      case 0: pv(int_c<0>{}, pbuf[0], nothing); break;
+      case 1: pv(int_c<1>{}, pbuf[1], nothing); break;
+      case 2: pv(int_c<2>{}, pbuf[0], nothing); break;
+      default: pv(int_c<3>{}, pbuf[1], nothing); break;
     }
   }
 
