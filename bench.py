@@ -38,9 +38,16 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8_e4m3": 5000.0, "f32": 157.3}
 ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fmha_fwd_kernel.h", "fmha_decode_kernel.h", "fmha_params.h", "fmha_combine.hip",
-                  "fmha_host.cpp", "fmha_fwd_bf16.hip", "fmha_fwd_f16.hip", "fmha_fwd_fp8.hip",
-                  "fmha_fwd_f32.hip"]
+# Sources a kernel's code depends on (the host plan, shared helpers and its own
+# header): a traffic measurement is used only while their hash is unchanged.
+_SHARED_SOURCES = ["fmha_fwd_kernel.h", "fmha_params.h", "fmha_host.cpp"]
+KERNEL_SOURCES = {
+    "fmha_decode_kernel": _SHARED_SOURCES + ["fmha_decode_kernel.h"],
+    "fmha_prefill_kernel": _SHARED_SOURCES + ["fmha_decode_kernel.h", "fmha_prefill_kernel.h"],
+    "fmha_prefill8_kernel": _SHARED_SOURCES + ["fmha_decode_kernel.h", "fmha_prefill_kernel.h",
+                                              "fmha_prefill8_kernel.h"],
+    "fmha_fwd_kernel": _SHARED_SOURCES,
+}
 
 
 # ---- workloads (shapes only; tensors come from fmha_synth) -----------------
@@ -103,9 +110,21 @@ def alg_flops(w):
     return 2 * (w["dqk"] + w["dv"]) * w["hq"] * pairs
 
 
-def kernel_source_hash():
+def kernel_name(kernel_id):
+    """Kernel family of a plan's kernel_id (dtype * 1000 + instance id)."""
+    i = kernel_id % 1000
+    if i >= 210:
+        return "fmha_prefill8_kernel"
+    if i >= 200:
+        return "fmha_prefill_kernel"
+    if i >= 100:
+        return "fmha_decode_kernel"
+    return "fmha_fwd_kernel"
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "split_kv_flash_fmha_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -324,7 +343,7 @@ def load_traffic(name):
             t = json.load(f).get(name)
     except (OSError, ValueError):
         return None
-    if not t or t.get("kernel_src_sha") != kernel_source_hash():
+    if not t or t.get("kernel") not in KERNEL_SOURCES or t.get("kernel_src_sha") != kernel_source_hash(t["kernel"]):
         return None
     return t.get("bytes_per_launch")
 
@@ -352,7 +371,7 @@ def summarize_pmc(fetch_csv, write_csv, workload, kernel_substr, copy_bytes):
     w_k, w_c, _ = read(write_csv)
     f_scale, w_scale = copy_bytes / (f_c * 1024), copy_bytes / (w_c * 1024)
     fetch_b, write_b = f_k * 1024 * f_scale, w_k * 1024 * w_scale
-    entry = dict(kernel_src_sha=kernel_source_hash(), kernel=kernel_substr, dispatches=n,
+    entry = dict(kernel_src_sha=kernel_source_hash(kernel_substr), kernel=kernel_substr, dispatches=n,
                  fetch_kib_raw=round(f_k, 3), write_kib_raw=round(w_k, 3),
                  copy_bytes=copy_bytes, copy_fetch_kib_raw=f_c, copy_write_kib_raw=w_c,
                  fetch_scale=round(f_scale, 5), write_scale=round(w_scale, 5),
@@ -429,8 +448,7 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = load_traffic(w["name"])
     roof["kernel_us"] = round(ms_kern * 1e3, 2)
-    roof["kernel"] = (("fmha_decode_kernel" if r.plan.kernel_id % 1000 >= 100 else "fmha_fwd_kernel")
-                      + (" (split partials)" if r.split else ""))
+    roof["kernel"] = kernel_name(r.plan.kernel_id) + (" (split partials)" if r.split else "")
 
     others = []
     if not args.no_others:

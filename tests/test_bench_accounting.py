@@ -54,3 +54,13 @@ def test_multi_gpu_request_exits(tmp_path):
     res = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                          text=True)
     assert res.returncode != 0 and "one GPU" in res.stderr
+
+
+def test_kernel_family_names():
+    """kernel_id = dtype * 1000 + instance id; instance ranges name the family."""
+    assert bench.kernel_name(2 * 1000 + 101) == "fmha_decode_kernel"
+    assert bench.kernel_name(1 * 1000 + 201) == "fmha_prefill_kernel"
+    assert bench.kernel_name(3 * 1000 + 211) == "fmha_prefill8_kernel"
+    assert bench.kernel_name(0 * 1000 + 7) == "fmha_fwd_kernel"
+    for name, files in bench.KERNEL_SOURCES.items():
+        assert len(bench.kernel_source_hash(name)) == 16 and files
