@@ -2,9 +2,10 @@
 // (sequence, kv head): the short cached-prefix shape of "[FlyDSL] Enable FP8
 // FMHA split-K for short cached-prefix queries" (description and measurement:
 // Q=70, Dq=Dk=192, Dv=128, per-tensor scales, split-K + combine) and fp8
-// prefill generally.  Same algorithm and pipeline as fmha_prefill_kernel.h
-// (32 query rows per wave, K one block ahead of V, QK of block n+1 issued
-// before the softmax of block n, lazy reference max), with fp8 operands:
+// prefill generally.  Same algorithm and software pipeline as
+// fmha_prefill_kernel.h (32 query rows per wave; iteration n runs PV(n-1) and
+// QK(n+1) on the MFMA pipe around the exponentials of block n; reference max
+// checked from the row sums), with fp8 operands:
 //
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_fp8_fp8.  A lane's 16-byte K read
 //    covers two k-steps: bytes 0-7 feed one MFMA, bytes 8-15 the next, and Q
@@ -16,18 +17,19 @@
 //    padded by 64 bytes so the two columns of one transpose-read pass fall in
 //    different banks.
 //  * O^T += V^T P^T with V^T from ds_read_b64_tr_b8 (8 keys x 16 dv per
-//    16-lane group) and P^T stored as e4m3 of p * 2^4.
-//  * Three LDS stages for K and for V: loads run two key blocks ahead of use,
-//    and each wave waits only for the loads it issued two iterations back.  With the reference max
-//    allowed to trail the running max by at most 2^4, p * 2^4 <= 2^8 stays
-//    inside e4m3's range; the factor is divided out with the V descale.
+//    16-lane group; one read per MFMA) and P^T stored as e4m3 of 8p.  The
+//    factor 8 is carried by l as well (it cancels in O and is taken out of the
+//    LSE); a row's 32 stored values sum to at most 448 unless the check sends
+//    the block to the slow path, so each stays inside e4m3's range.
+//  * Rings of four K stages and three V stages in LDS; K runs three blocks and
+//    V two blocks ahead of use.
 #pragma once
 #include "fmha_prefill_kernel.h"
 
 namespace fmha {
 
-constexpr float kRescaleSlack8 = 4.0f;
-constexpr float kPScale8 = 16.0f;
+constexpr float kPScale8Log2 = 3.0f;  // P stored as e4m3 of 2^3 p
+constexpr float kSumLimit8 = 448.0f;  // e4m3's largest finite value
 
 __device__ __forceinline__ f32x16 mfma32_fp8(f32x16 acc, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1) {
   const u32x2 a = {a0, a1}, b = {b0, b1};
@@ -46,26 +48,29 @@ struct Pf8Cfg {
   static constexpr int KP2 = DQK / 32;   // 16-byte Q/K chunks per lane half (2 k-steps each)
   static constexpr int NT = BN / 32;
   static constexpr int TV = DV / 32;
+  static constexpr int NG = 2 * NT;      // PV groups of 16 keys
   static constexpr int KCOLS = DQK / 16;
   static constexpr int VCOLS = DV / 16;
   static constexpr int KCP = BN * 16;        // K column pitch
   static constexpr int VCP = BN * 16 + 64;   // V column pitch
   static constexpr int KTILE = KCOLS * KCP;
   static constexpr int VTILE = VCOLS * VCP;
-  static constexpr int NS = 3;                          // LDS ring depth (K and V)
+  static constexpr int NSK = 4;                         // K ring stages
+  static constexpr int NSV = 3;                         // V ring stages
   static constexpr int KL = (KCOLS + NWM - 1) / NWM;    // K column loads per wave per block
   static constexpr int VL = (VCOLS + NWM - 1) / NWM;    // V column loads per wave per block
-  static constexpr int LDS = NS * (KTILE + VTILE);
+  static constexpr int LDS = NSK * KTILE + NSV * VTILE;
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
+  static_assert(KTILE % 256 == 0 && VTILE % 64 == 0, "stage offsets");
 };
 
 template <class C>
 __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wm = tid >> 6;
+  const int wm = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;
   const int lr = lane & 31;
 
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   float scale_log2 = p.scale_log2;
   if (p.q_descale) scale_log2 *= *p.q_descale;
   if (p.k_descale) scale_log2 *= *p.k_descale;
-  const float v_scale = (p.v_descale ? *p.v_descale : 1.0f) * (1.0f / kPScale8);
+  const float v_scale = p.v_descale ? *p.v_descale : 1.0f;
 
   // Q^T: chunk pair s, lane half h holds Q bytes [32s + 16h, +16): bytes 0-7
   // are the k-slots of MFMA 2s, bytes 8-15 those of MFMA 2s+1
@@ -117,8 +122,8 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
                        (int64_t)hq * p.q_sh;
 #pragma unroll
     for (int s = 0; s < C::KP2; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qf[s] = row_ok ? *(const u32x4*)(qrow + 32 * s + 16 * hl) : z;
+      qf[s] = *(const u32x4*)(qrow + 32 * s + 16 * hl);
+      if (!row_ok) qf[s] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -145,24 +150,30 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // per-lane constant parts of the LDS addresses
-  const int k_rd = hl * C::KCP + lr * 16;  // + (2s)*KCP + 32u*16
+  // per-lane parts of the LDS read addresses (stage offsets added per block)
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t k_rd = lds0 + (uint32_t)(hl * C::KCP + lr * 16);  // + 2s*KCP + 32u*16
   const int gq = (lane >> 4) & 1, i16 = lane & 15, e8 = i16 >> 1, jh = i16 & 1;
-  const int v_rd = gq * C::VCP + (8 * (e8 >> 2) + 4 * hl + (e8 & 3)) * 16 + 8 * jh;  // + 2t*VCP + (32u+16m)*16
+  const uint32_t v_rd = lds0 + (uint32_t)(C::NSK * C::KTILE + gq * C::VCP +
+                                          (8 * (e8 >> 2) + 4 * hl + (e8 & 3)) * 16 + 8 * jh);  // + 2t*VCP + (32u+16m)*16
 
   // zero the LDS once so no slot is read uninitialised
   for (int i = tid * 16; i < C::LDS; i += C::NTHR * 16) *(u32x4*)(smem + i) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  // one 1 KiB load = 16-byte column c of the 64 rows of a block (lane = row);
-  // rows past the key range read as zero (descriptor ends at the last key),
-  // and a block that starts past it gets an empty descriptor (nothing is
-  // fetched).  Every wave issues exactly KL K and VL V loads per block (the
+  // One 1 KiB load = 16-byte column c of the 64 rows of a block (lane = row).
+  // The descriptor covers the rows of the block the tile needs (rows past them
+  // read as zero; a block past them gets an empty descriptor and fetches
+  // nothing).  Every wave issues exactly KL K and VL V loads per block (the
   // last column repeated where the columns do not divide evenly; identical
   // bytes), so the loads a wave has in flight are a compile-time count.
-  auto issue_k = [&](int j0, int st) {
-    const int64_t nb = j0 < j_end ? (int64_t)min(ke - 1 - j0, C::BN) * p.k_st + C::DQK : 0;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)j0 * p.k_st, nb);
+  auto block_rsrc = [&](const char* base, int64_t st, int jb, int rowb) {
+    const int rows_left = min(j_end - jb, C::BN);
+    const int nb = rows_left > 0 ? (rows_left - 1) * (int)st + rowb : 0;
+    return make_rsrc(base + (int64_t)jb * st, nb);
+  };
+  auto issue_k = [&](int jb, int st) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, p.k_st, jb, C::DQK);
     char* dst = smem + st * C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::KL; ++i) {
@@ -170,69 +181,137 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
       buffer_to_lds16(rk, dst + c * C::KCP, lane * (int)p.k_st + c * 16);
     }
   };
-  auto issue_v = [&](int j0, int st) {
-    const int64_t nb = j0 < j_end ? (int64_t)min(ke - 1 - j0, C::BN) * p.v_st + C::DV : 0;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)j0 * p.v_st, nb);
-    char* dst = smem + C::NS * C::KTILE + st * C::VTILE;
+  auto issue_v = [&](int jb, int st) {
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, p.v_st, jb, C::DV);
+    char* dst = smem + C::NSK * C::KTILE + st * C::VTILE;
 #pragma unroll
     for (int i = 0; i < C::VL; ++i) {
       const int c = min(wm + i * C::NWM, C::VCOLS - 1);
       buffer_to_lds16(rv, dst + c * C::VCP, lane * (int)p.v_st + c * 16);
     }
   };
-  auto qk = [&](f32x16 (&sd)[C::NT], int st) {
-    const char* Ks = smem + st * C::KTILE + k_rd;
-#pragma unroll
-    for (int u = 0; u < C::NT; ++u)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sd[u][e] = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < C::KP2; ++s2) {
-      u32x4 kf[C::NT];
-#pragma unroll
-      for (int u = 0; u < C::NT; ++u) kf[u] = *(const u32x4*)(Ks + 2 * s2 * C::KCP + 32 * u * 16);
-#pragma unroll
-      for (int u = 0; u < C::NT; ++u) {
-        sd[u] = mfma32_fp8(sd[u], kf[u].x, kf[u].y, qf[s2].x, qf[s2].y);
-        sd[u] = mfma32_fp8(sd[u], kf[u].z, kf[u].w, qf[s2].z, qf[s2].w);
-      }
-    }
+  auto wait_loads = [](auto N_) {
+    constexpr int n = decltype(N_)::value;
+    static_assert(n < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
   };
-  // at most KL + VL of this wave's loads (one block's K and V) in flight;
-  // loads retire in order, so everything issued before them has landed
-  constexpr int kInFlight = C::KL + C::VL;
-  static_assert(kInFlight < 64, "vmcnt");
-  auto wait_older_loads = [] {
-    __builtin_amdgcn_s_waitcnt((kInFlight & 15) | ((kInFlight >> 4) << 14) | (7 << 4) | (15 << 8));
-  };
-  const uint32_t va0 = lds_addr(smem) + (uint32_t)v_rd;
 
-  // Ring of three stages: K(b) in K stage b%3, V(b) in V stage b%3.
-  // Iteration it waits for K(it+1) and V(it), issues K(it+3) and V(it+2) and
-  // computes QK(it+1) and PV(it): loads run two blocks ahead of their use.
-  f32x16 s_cur[C::NT], s_nxt[C::NT];
+  // P of a key block as e4m3 of 8p, two words per PV group g (keys 16g..16g+15)
+  u32x2 pbuf[2][C::NG];
+
+  // O^T += V^T P^T from V stage vst: MFMA n = (group g, tile t) reads its V^T
+  // fragment (lane 2e+jh of 16-lane group (hl, gq): key row
+  // 32u+16m+8(e/4)+4hl+e%4, dv bytes 32t+16gq+8jh..+7; it receives dv column lr
+  // of those 8 keys) VR reads ahead; `between(n)` is VALU work after MFMA n.
+  auto pv = [&](int vst, const u32x2 (&pb)[C::NG], auto&& between) {
+    constexpr int NM = C::NG * C::TV;
+    constexpr int VR = 8;
+    const uint32_t vb = v_rd + (uint32_t)(vst * C::VTILE);
+    i32x2 vr[VR];
+    auto read_frag = [&](auto N_) {
+      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV, u = g >> 1, m = g & 1;
+      vr[n % VR] = lds_tr8<2 * t * C::VCP + (32 * u + 16 * m) * 16>(vb);
+    };
+    static_for<VR - 1>([&](auto N_) {
+      if constexpr (decltype(N_)::value < NM) read_frag(N_);
+    });
+    static_for<NM>([&](auto N_) {
+      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
+      if constexpr (n + VR - 1 < NM) read_frag(int_c<n + VR - 1>{});
+      lgkm_wait<(NM - 1 - n < VR - 1 ? NM - 1 - n : VR - 1)>();
+      tie(vr[n % VR]);
+      acc[t] = mfma32_fp8(acc[t], (uint32_t)vr[n % VR].x, (uint32_t)vr[n % VR].y, pb[g].x, pb[g].y);
+      between(int_c<n>{});
+    });
+  };
+
+  // S^T = K Q^T from K stage kst into sd: 16-byte read r = (tile u, chunk pair
+  // s2) feeds MFMAs 2r and 2r+1; reads run KR - 1 ahead; `between(n)` is VALU
+  // work after MFMA n.
+  auto qk = [&](int kst, f32x16 (&sd)[C::NT], auto&& between) {
+    constexpr int NR = C::NT * C::KP2;
+    constexpr int KR = 4;
+    const uint32_t kbs = k_rd + (uint32_t)(kst * C::KTILE);
+    u32x4 kf[KR];
+    auto read_k = [&](auto R_) {
+      constexpr int rr = decltype(R_)::value, u = rr / C::KP2, s2 = rr % C::KP2;
+      kf[rr % KR] = lds_b128<2 * s2 * C::KCP + 32 * u * 16>(kbs);
+    };
+    static_for<KR - 1>([&](auto R_) {
+      if constexpr (decltype(R_)::value < NR) read_k(R_);
+    });
+    static_for<NR>([&](auto R_) {
+      constexpr int rr = decltype(R_)::value, u = rr / C::KP2, s2 = rr % C::KP2;
+      if constexpr (rr + KR - 1 < NR) read_k(int_c<rr + KR - 1>{});
+      lgkm_wait<(NR - 1 - rr < KR - 1 ? NR - 1 - rr : KR - 1)>();
+      tie(kf[rr % KR]);
+      if constexpr (s2 == 0) {
+        f32x16 z;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = 0.f;
+        sd[u] = mfma32_fp8(z, kf[rr % KR].x, kf[rr % KR].y, qf[s2].x, qf[s2].y);
+      } else {
+        sd[u] = mfma32_fp8(sd[u], kf[rr % KR].x, kf[rr % KR].y, qf[s2].x, qf[s2].y);
+      }
+      between(int_c<2 * rr>{});
+      sd[u] = mfma32_fp8(sd[u], kf[rr % KR].z, kf[rr % KR].w, qf[s2].z, qf[s2].w);
+      between(int_c<2 * rr + 1>{});
+    });
+  };
+  auto nothing = [](auto) {};
+
+  // exponentials of a block: word w = elements 4w..4w+3 of the lane's S (tile
+  // w / 4, elements 4(w % 4)..), stored as e4m3 of 8p; rs sums the 8p
+  constexpr int NPV = C::NG * C::TV, NQK = 2 * C::NT * C::KP2;  // MFMAs per phase
+  constexpr int NWD = 4 * C::NT;                                // words per block
+  auto exp_word = [&](const f32x16 (&sd)[C::NT], u32x2 (&pb)[C::NG], float nb, float& rs, auto W_) {
+    constexpr int w = decltype(W_)::value, u = w >> 2, e0 = 4 * (w & 3);
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = fast_exp2(__builtin_fmaf(sd[u][e0 + i], scale_log2, nb));
+    uint32_t word = pack_fp8x4(q[0], q[1], q[2], q[3]);
+    tie(word);
+    pb[w >> 1][w & 1] = word;
+    rs += (q[0] + q[1]) + (q[2] + q[3]);
+    tie(rs);
+  };
+  auto words_upto = [](int k) { return (k * NWD) / (NPV + NQK); };
+
+  // Rings: K(b) in K stage b % 4, V(b) in V stage b % 3.  Iteration it issues
+  // K(it+4) and V(it+1) and needs K(it+1) (QK) and V(it-1) (PV): only the
+  // previous iteration's loads may still be in flight.  The prologue issues in
+  // the order iterations -4..-1 would (empty loads for V(-3)..V(-1)).
+  f32x16 sbuf[2][C::NT];
+  const int jlast = j_begin + n_iter * C::BN;
   if (n_iter > 0) {
     issue_k(j_begin, 0);
-    issue_v(j_begin, 0);
+    issue_v(jlast, 1);  // empty
     issue_k(j_begin + C::BN, 1);
+    issue_v(jlast, 1);  // empty
     issue_k(j_begin + 2 * C::BN, 2);
-    issue_v(j_begin + C::BN, 1);
-    wait_older_loads();  // K(0), V(0), K(1) landed
+    issue_v(jlast, 1);  // empty
+    issue_k(j_begin + 3 * C::BN, 3);
+    issue_v(j_begin, 0);
+    wait_loads(int_c<3 * C::KL + 4 * C::VL>{});  // K(0) landed
     block_barrier();
-    qk(s_cur, 0);
+    qk(0, sbuf[0], nothing);
   }
 
-  int st = 0;  // it % 3
-  for (int it = 0; it < n_iter; ++it) {
+  int kst = 1;  // (it + 1) % 4: K stage of QK(it+1)
+  int vst = 2;  // (it - 1) % 3: V stage of PV(it-1)
+  // SB = it % 2 at compile time (S and P buffers stay in registers)
+  auto body = [&](auto SB_, auto FIRST_, int it) {
+    constexpr int SB = decltype(SB_)::value;
+    constexpr bool FIRST = decltype(FIRST_)::value != 0;
     const int j0 = j_begin + it * C::BN;
-    const int st1 = st == 2 ? 0 : st + 1;
-    const int st2 = st1 == 2 ? 0 : st1 + 1;
-    wait_older_loads();
-    block_barrier();  // K(it+1), V(it) in LDS everywhere; stages of K(it), V(it-1) free
-    issue_k(j0 + 3 * C::BN, st);
-    issue_v(j0 + 2 * C::BN, st2);
-    if (it + 1 < n_iter) qk(s_nxt, st1);
-    f32x16 (&s)[C::NT] = s_cur;
+    wait_loads(int_c<C::KL + C::VL>{});
+    block_barrier();  // K(it+1), V(it-1) in LDS everywhere; K stage it%4, V stage (it+1)%3 free
+    const int kst_free = kst == 0 ? 3 : kst - 1;  // it % 4
+    const int vst_free = vst == 0 ? 2 : vst - 1;              // (it + 1) % 3 == (vst + 2) % 3
+    issue_k(j0 + 4 * C::BN, kst_free);
+    issue_v(j0 + C::BN, vst_free);
+    f32x16 (&s)[C::NT] = sbuf[SB];
+    u32x2 (&pc)[C::NG] = pbuf[SB];
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
     if (!full) {
@@ -244,80 +323,71 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
           if (j < my_lo || j > my_hi) s[u][e] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    auto row_max = [&]() {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < C::NT; ++u)
+      for (int u = 0; u < C::NT; ++u)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_blk = mx * scale_log2;
-    if (__any(m_blk > m_run + kRescaleSlack8)) {
-      const float m_new = fmaxf(m_run, m_blk);
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+      return max_halves(mx) * scale_log2;
+    };
+    if constexpr (FIRST) m_run = row_max();
+    const float nbase = kPScale8Log2 - (m_run == -INFINITY ? 0.f : m_run);
+    float rs = 0.f;
+    auto slot = [&](auto K_) {
+      constexpr int k = decltype(K_)::value;
+      static_for<words_upto(k + 1) - words_upto(k)>([&](auto W_) {
+        exp_word(s, pc, nbase, rs, int_c<words_upto(k) + decltype(W_)::value>{});
+      });
+    };
+    if constexpr (!FIRST) {
+      pv(vst, pbuf[SB ^ 1], [&](auto N_) { slot(N_); });
+    } else {
+      static_for<NPV>([&](auto N_) { slot(N_); });
+    }
+    qk(kst, sbuf[SB ^ 1], [&](auto N_) { slot(int_c<NPV + decltype(N_)::value>{}); });
+    // reference check: a stored 8p above e4m3's range, or a row with keys in
+    // this block and no reference yet, sends the block to the slow path
+    const bool has_keys = my_lo <= j0 + C::BN - 1 && my_hi >= j0 && my_lo <= my_hi;
+    if (__any(rs > kSumLimit8 || (m_run == -INFINITY && has_keys))) {
+      const float m_new = fmaxf(m_run, row_max());
       const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < C::TV; ++t) acc[t] *= alpha;
       m_run = m_new;
-    }
-    const float nbase = -(m_run == -INFINITY ? 0.f : m_run);
-    float rs = 0.f;
-#pragma unroll
-    for (int u = 0; u < C::NT; ++u) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(__builtin_fmaf(s[u][e], scale_log2, nbase));
-        s[u][e] = pe;
-        rs += pe;
-      }
+      const float nb2 = kPScale8Log2 - (m_run == -INFINITY ? 0.f : m_run);
+      rs = 0.f;
+      static_for<NWD>([&](auto W_) { exp_word(s, pc, nb2, rs, W_); });
     }
     l_run += rs;
-    // O^T += V^T P^T: group g = (u, m) covers keys 32u+16m+{0..15}.  Lane
-    // 2e+jh of 16-lane group (hl, gq) reads key row 32u+16m+8(e/4)+4hl+e%4,
-    // dv bytes 32t+16gq+8jh..+7, and receives dv column lr of those 8 keys.
-    // The reads of group g+1 are in flight during group g's MFMAs.
-    const uint32_t va = va0 + (uint32_t)(st * C::VTILE);
-    i32x2 vr[2][C::TV];
-    auto read_group = [&](auto G_) {
-      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
-      static_for<C::TV>([&](auto T_) {
-        constexpr int t = decltype(T_)::value;
-        vr[g & 1][t] = lds_tr8<C::NS * C::KTILE + 2 * t * C::VCP + (32 * u + 16 * m) * 16>(va);
-      });
-    };
-    read_group(int_c<0>{});
-    static_for<2 * C::NT>([&](auto G_) {
-      constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
-      const float ps = kPScale8;
-      const uint32_t p0 =
-          pack_fp8x4(s[u][8 * m + 0] * ps, s[u][8 * m + 1] * ps, s[u][8 * m + 2] * ps, s[u][8 * m + 3] * ps);
-      const uint32_t p1 =
-          pack_fp8x4(s[u][8 * m + 4] * ps, s[u][8 * m + 5] * ps, s[u][8 * m + 6] * ps, s[u][8 * m + 7] * ps);
-      if constexpr (g + 1 < 2 * C::NT) {
-        read_group(int_c<g + 1>{});
-        lgkm_wait<C::TV>();
-      } else {
-        lgkm_wait<0>();
-      }
-      static_for<C::TV>([&](auto T_) {
-        constexpr int t = decltype(T_)::value;
-        tie(vr[g & 1][t]);
-        acc[t] = mfma32_fp8(acc[t], (uint32_t)vr[g & 1][t].x, (uint32_t)vr[g & 1][t].y, p0, p1);
-      });
-    });
-#pragma unroll
-    for (int u = 0; u < C::NT; ++u) s_cur[u] = s_nxt[u];
-    st = st1;
+    kst = kst == 3 ? 0 : kst + 1;
+    vst = vst == 2 ? 0 : vst + 1;
+  };
+
+  if (n_iter > 0) {
+    body(int_c<0>{}, int_c<1>{}, 0);
+    for (int it = 1; it < n_iter; ++it) {
+      body(int_c<1>{}, int_c<0>{}, it);
+      if (++it >= n_iter) break;
+      body(int_c<0>{}, int_c<0>{}, it);
+    }
+    // PV of the last block (V stage (n_iter-1) % 3 == vst, P of block n_iter-1)
+    __builtin_amdgcn_s_waitcnt(0);
+    block_barrier();
+    if ((n_iter - 1) & 1)
+      pv(vst, pbuf[1], nothing);
+    else
+      pv(vst, pbuf[0], nothing);
   }
-  // the ring's last loads (empty descriptors) must retire before the
-  // workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
   const bool live = l_tot > 0.f;
   const float inv = live ? v_scale / l_tot : 0.f;
-  const float lse_v = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // l_run and acc both count 2^kPScale8Log2 * p: the factor cancels in O
+  const float lse_v = live ? (m_run + __log2f(l_tot) - kPScale8Log2) * kLn2 : -INFINITY;
   if (S > 1) {
     const int64_t tglob = (int64_t)q_off + iq;
     float* op = p.o_part + (((int64_t)split * p.total_q + tglob) * p.hq + hq) * C::DV;
