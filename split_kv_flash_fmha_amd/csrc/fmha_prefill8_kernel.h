@@ -7,17 +7,20 @@
 // QK(n+1) on the MFMA pipe around the exponentials of block n; reference max
 // checked from the row sums), with fp8 operands:
 //
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_fp8_fp8.  A lane's 16-byte K read
-//    covers two k-steps: bytes 0-7 feed one MFMA, bytes 8-15 the next, and Q
-//    is loaded with the same byte mapping.
+//  * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 (64 d per MFMA): lane half h
+//    of d chunk c carries d = 64c + 32h + b in byte b, for K (two 16-byte LDS
+//    reads) and for Q (held in registers) alike.
 //  * K and V blocks sit in LDS "chunk-major": 16-byte column c of all BN rows
 //    is contiguous (BN rows x 16 bytes), which suits any row length (192-byte
 //    K rows) and makes each 1 KiB buffer->LDS load one column of 64 rows.  The
 //    16-byte K reads of 16 consecutive rows are contiguous; V columns are
 //    padded by 64 bytes so the two columns of one transpose-read pass fall in
 //    different banks.
-//  * O^T += V^T P^T with V^T from ds_read_b64_tr_b8 (8 keys x 16 dv per
-//    16-lane group; one read per MFMA) and P^T stored as e4m3 of 8p.  The
+//  * O^T += V^T P^T on the same MFMA (64 keys per MFMA): byte 16u+4j+i of
+//    lane half h carries key 32u+8j+4h+i, which is where the S^T output puts
+//    that key, so P^T is packed straight from it; V^T comes from four
+//    ds_read_b64_tr_b8 (8 keys x 16 dv per 16-lane group) in the same key
+//    order.  P^T is stored as e4m3 of 8p.  The
 //    factor 8 is carried by l as well (it cancels in O and is taken out of the
 //    LSE); a row's 32 stored values sum to at most 448 unless the check sends
 //    the block to the slow path, so each stays inside e4m3's range.
@@ -31,10 +34,16 @@ namespace fmha {
 constexpr float kPScale8Log2 = 3.0f;  // P stored as e4m3 of 2^3 p
 constexpr float kSumLimit8 = 448.0f;  // e4m3's largest finite value
 
-__device__ __forceinline__ f32x16 mfma32_fp8(f32x16 acc, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1) {
-  const u32x2 a = {a0, a1}, b = {b0, b1};
-  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), acc, 0,
-                                                    0, 0);
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_f32_32x32x64_f8f6f4 with e4m3 A and B (format code 0, no scaling).
+// Operand lane l: row (A) / column (B) l % 32; its 32 bytes are the k-slots
+// of lane half l / 32, byte b of A pairing with byte b of B (the kernel picks
+// which key or d each byte carries, the same on both sides).
+__device__ __forceinline__ f32x16 mfma64_fp8(f32x16 acc, u32x8 a, u32x8 b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                         acc, 0, 0, 0, 0, 0, 0);
 }
 
 template <int DQK_, int DV_, int NWM_>
@@ -45,7 +54,7 @@ struct Pf8Cfg {
   static constexpr int BN = 64;          // keys per block: one 1 KiB load per 16-byte column
   static constexpr int NTHR = 64 * NWM;
   static constexpr int ROWS = 32 * NWM;
-  static constexpr int KP2 = DQK / 32;   // 16-byte Q/K chunks per lane half (2 k-steps each)
+  static constexpr int KC = DQK / 64;    // 64-deep d chunks of QK (one MFMA each)
   static constexpr int NT = BN / 32;
   static constexpr int TV = DV / 32;
   static constexpr int NG = 2 * NT;      // PV groups of 16 keys
@@ -60,7 +69,7 @@ struct Pf8Cfg {
   static constexpr int KL = (KCOLS + NWM - 1) / NWM;    // K column loads per wave per block
   static constexpr int VL = (VCOLS + NWM - 1) / NWM;    // V column loads per wave per block
   static constexpr int LDS = NSK * KTILE + NSV * VTILE;
-  static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
+  static_assert(DQK % 64 == 0 && DV % 32 == 0, "head dims");
   static_assert(KTILE % 256 == 0 && VTILE % 64 == 0, "stage offsets");
 };
 
@@ -114,16 +123,17 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   if (p.k_descale) scale_log2 *= *p.k_descale;
   const float v_scale = p.v_descale ? *p.v_descale : 1.0f;
 
-  // Q^T: chunk pair s, lane half h holds Q bytes [32s + 16h, +16): bytes 0-7
-  // are the k-slots of MFMA 2s, bytes 8-15 those of MFMA 2s+1
-  u32x4 qf[C::KP2];
+  // Q^T (B operand): d chunk c, lane half h holds Q bytes [64c + 32h, +32)
+  u32x8 qf[C::KC];
   {
     const char* qrow = p.q + (p.cu_q ? (int64_t)(q_off + iq) * p.q_st : (int64_t)b * p.q_sb + (int64_t)iq * p.q_st) +
                        (int64_t)hq * p.q_sh;
 #pragma unroll
-    for (int s = 0; s < C::KP2; ++s) {
-      qf[s] = *(const u32x4*)(qrow + 32 * s + 16 * hl);
-      if (!row_ok) qf[s] = u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < C::KC; ++c) {
+      const u32x4 lo = *(const u32x4*)(qrow + 64 * c + 32 * hl);
+      const u32x4 hi = *(const u32x4*)(qrow + 64 * c + 32 * hl + 16);
+      qf[c] = u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (!row_ok) qf[c] = u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     }
   }
 
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
 
   // per-lane parts of the LDS read addresses (stage offsets added per block)
   const uint32_t lds0 = lds_addr(smem);
-  const uint32_t k_rd = lds0 + (uint32_t)(hl * C::KCP + lr * 16);  // + 2s*KCP + 32u*16
+  const uint32_t k_rd = lds0 + (uint32_t)(2 * hl * C::KCP + lr * 16);  // + 4c*KCP (+KCP) + 32u*16
   const int gq = (lane >> 4) & 1, i16 = lane & 15, e8 = i16 >> 1, jh = i16 & 1;
   const uint32_t v_rd = lds0 + (uint32_t)(C::NSK * C::KTILE + gq * C::VCP +
                                           (8 * (e8 >> 2) + 4 * hl + (e8 & 3)) * 16 + 8 * jh);  // + 2t*VCP + (32u+16m)*16
@@ -196,82 +206,102 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
   };
 
-  // P of a key block as e4m3 of 8p, two words per PV group g (keys 16g..16g+15)
-  u32x2 pbuf[2][C::NG];
+  // P^T of a key block as e4m3 of 8p: the 32-byte B operand of the PV MFMA
+  static_assert(C::BN == 64, "one PV MFMA per block and dv tile");
+  u32x8 pbuf[2];
 
-  // O^T += V^T P^T from V stage vst: MFMA n = (group g, tile t) reads its V^T
-  // fragment (lane 2e+jh of 16-lane group (hl, gq): key row
-  // 32u+16m+8(e/4)+4hl+e%4, dv bytes 32t+16gq+8jh..+7; it receives dv column lr
-  // of those 8 keys) VR reads ahead; `between(n)` is VALU work after MFMA n.
-  auto pv = [&](int vst, const u32x2 (&pb)[C::NG], auto&& between) {
-    constexpr int NM = C::NG * C::TV;
-    constexpr int VR = 8;
+  // O^T += V^T P^T from V stage vst: MFMA t (dv tile t) takes V^T from four
+  // transpose reads, read (t, g) for key group g = (u, m): lane 2e+jh of
+  // 16-lane group (hl, gq) reads key row 32u+16m+8(e/4)+4hl+e%4, dv bytes
+  // 32t+16gq+8jh..+7, and receives dv column lr of those 8 keys (bytes 8g..8g+7
+  // of its operand).  Reads run two MFMAs ahead; `between(t)` is VALU work
+  // after MFMA t.
+  auto pv = [&](int vst, const u32x8& pb, auto&& between) {
+    constexpr int NM = C::TV;
     const uint32_t vb = v_rd + (uint32_t)(vst * C::VTILE);
-    i32x2 vr[VR];
-    auto read_frag = [&](auto N_) {
-      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV, u = g >> 1, m = g & 1;
-      vr[n % VR] = lds_tr8<2 * t * C::VCP + (32 * u + 16 * m) * 16>(vb);
+    i32x2 vr[3][4];
+    auto read_frag = [&](auto T_) {
+      constexpr int t = decltype(T_)::value;
+      static_for<4>([&](auto G_) {
+        constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
+        vr[t % 3][g] = lds_tr8<2 * t * C::VCP + (32 * u + 16 * m) * 16>(vb);
+      });
     };
-    static_for<VR - 1>([&](auto N_) {
-      if constexpr (decltype(N_)::value < NM) read_frag(N_);
-    });
-    static_for<NM>([&](auto N_) {
-      constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
-      if constexpr (n + VR - 1 < NM) read_frag(int_c<n + VR - 1>{});
-      lgkm_wait<(NM - 1 - n < VR - 1 ? NM - 1 - n : VR - 1)>();
-      tie(vr[n % VR]);
-      acc[t] = mfma32_fp8(acc[t], (uint32_t)vr[n % VR].x, (uint32_t)vr[n % VR].y, pb[g].x, pb[g].y);
-      between(int_c<n>{});
+    read_frag(int_c<0>{});
+    if constexpr (NM > 1) read_frag(int_c<1>{});
+    static_for<NM>([&](auto T_) {
+      constexpr int t = decltype(T_)::value;
+      if constexpr (t + 2 < NM) {
+        read_frag(int_c<t + 2>{});
+        lgkm_wait<8>();
+      } else if constexpr (t + 1 < NM) {
+        lgkm_wait<4>();
+      } else {
+        lgkm_wait<0>();
+      }
+      static_for<4>([&](auto G_) { tie(vr[t % 3][decltype(G_)::value]); });
+      const u32x8 va = {(uint32_t)vr[t % 3][0].x, (uint32_t)vr[t % 3][0].y, (uint32_t)vr[t % 3][1].x,
+                        (uint32_t)vr[t % 3][1].y, (uint32_t)vr[t % 3][2].x, (uint32_t)vr[t % 3][2].y,
+                        (uint32_t)vr[t % 3][3].x, (uint32_t)vr[t % 3][3].y};
+      acc[t] = mfma64_fp8(acc[t], va, pb);
+      between(int_c<t>{});
     });
   };
 
-  // S^T = K Q^T from K stage kst into sd: 16-byte read r = (tile u, chunk pair
-  // s2) feeds MFMAs 2r and 2r+1; reads run KR - 1 ahead; `between(n)` is VALU
-  // work after MFMA n.
+  // S^T = K Q^T from K stage kst into sd: MFMA n = (tile u, d chunk c) takes
+  // K columns 4c+2h and 4c+2h+1 (32 bytes) of rows 32u + lr; reads run two
+  // MFMAs ahead; `between(n)` is VALU work after MFMA n.
   auto qk = [&](int kst, f32x16 (&sd)[C::NT], auto&& between) {
-    constexpr int NR = C::NT * C::KP2;
-    constexpr int KR = 4;
+    constexpr int NM = C::NT * C::KC;
     const uint32_t kbs = k_rd + (uint32_t)(kst * C::KTILE);
-    u32x4 kf[KR];
-    auto read_k = [&](auto R_) {
-      constexpr int rr = decltype(R_)::value, u = rr / C::KP2, s2 = rr % C::KP2;
-      kf[rr % KR] = lds_b128<2 * s2 * C::KCP + 32 * u * 16>(kbs);
+    u32x4 kf[3][2];
+    auto read_k = [&](auto N_) {
+      constexpr int n = decltype(N_)::value, u = n / C::KC, c = n % C::KC;
+      kf[n % 3][0] = lds_b128<4 * c * C::KCP + 32 * u * 16>(kbs);
+      kf[n % 3][1] = lds_b128<(4 * c + 1) * C::KCP + 32 * u * 16>(kbs);
     };
-    static_for<KR - 1>([&](auto R_) {
-      if constexpr (decltype(R_)::value < NR) read_k(R_);
-    });
-    static_for<NR>([&](auto R_) {
-      constexpr int rr = decltype(R_)::value, u = rr / C::KP2, s2 = rr % C::KP2;
-      if constexpr (rr + KR - 1 < NR) read_k(int_c<rr + KR - 1>{});
-      lgkm_wait<(NR - 1 - rr < KR - 1 ? NR - 1 - rr : KR - 1)>();
-      tie(kf[rr % KR]);
-      if constexpr (s2 == 0) {
+    read_k(int_c<0>{});
+    if constexpr (NM > 1) read_k(int_c<1>{});
+    static_for<NM>([&](auto N_) {
+      constexpr int n = decltype(N_)::value, u = n / C::KC, c = n % C::KC;
+      if constexpr (n + 2 < NM) {
+        read_k(int_c<n + 2>{});
+        lgkm_wait<4>();
+      } else if constexpr (n + 1 < NM) {
+        lgkm_wait<2>();
+      } else {
+        lgkm_wait<0>();
+      }
+      tie(kf[n % 3][0]);
+      tie(kf[n % 3][1]);
+      const u32x8 ka = {kf[n % 3][0].x, kf[n % 3][0].y, kf[n % 3][0].z, kf[n % 3][0].w,
+                        kf[n % 3][1].x, kf[n % 3][1].y, kf[n % 3][1].z, kf[n % 3][1].w};
+      if constexpr (c == 0) {
         f32x16 z;
 #pragma unroll
         for (int e = 0; e < 16; ++e) z[e] = 0.f;
-        sd[u] = mfma32_fp8(z, kf[rr % KR].x, kf[rr % KR].y, qf[s2].x, qf[s2].y);
+        sd[u] = mfma64_fp8(z, ka, qf[c]);
       } else {
-        sd[u] = mfma32_fp8(sd[u], kf[rr % KR].x, kf[rr % KR].y, qf[s2].x, qf[s2].y);
+        sd[u] = mfma64_fp8(sd[u], ka, qf[c]);
       }
-      between(int_c<2 * rr>{});
-      sd[u] = mfma32_fp8(sd[u], kf[rr % KR].z, kf[rr % KR].w, qf[s2].z, qf[s2].w);
-      between(int_c<2 * rr + 1>{});
+      between(int_c<n>{});
     });
   };
   auto nothing = [](auto) {};
 
-  // exponentials of a block: word w = elements 4w..4w+3 of the lane's S (tile
-  // w / 4, elements 4(w % 4)..), stored as e4m3 of 8p; rs sums the 8p
-  constexpr int NPV = C::NG * C::TV, NQK = 2 * C::NT * C::KP2;  // MFMAs per phase
-  constexpr int NWD = 4 * C::NT;                                // words per block
-  auto exp_word = [&](const f32x16 (&sd)[C::NT], u32x2 (&pb)[C::NG], float nb, float& rs, auto W_) {
+  // exponentials of a block: word w = elements 4(w % 4).. of the lane's S tile
+  // w / 4 (keys 32u+8j+4h+i, i < 4, for u = w / 4, j = w % 4), stored as e4m3
+  // of 8p in bytes 4w..4w+3 of the PV B operand; rs sums the 8p
+  constexpr int NPV = C::TV, NQK = C::NT * C::KC;  // MFMAs per phase
+  constexpr int NWD = 4 * C::NT;                   // words per block
+  auto exp_word = [&](const f32x16 (&sd)[C::NT], u32x8& pb, float nb, float& rs, auto W_) {
     constexpr int w = decltype(W_)::value, u = w >> 2, e0 = 4 * (w & 3);
     float q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) q[i] = fast_exp2(__builtin_fmaf(sd[u][e0 + i], scale_log2, nb));
     uint32_t word = pack_fp8x4(q[0], q[1], q[2], q[3]);
     tie(word);
-    pb[w >> 1][w & 1] = word;
+    pb[w] = word;
     rs += (q[0] + q[1]) + (q[2] + q[3]);
     tie(rs);
   };
@@ -311,7 +341,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     issue_k(j0 + 4 * C::BN, kst_free);
     issue_v(j0 + C::BN, vst_free);
     f32x16 (&s)[C::NT] = sbuf[SB];
-    u32x2 (&pc)[C::NG] = pbuf[SB];
+    u32x8& pc = pbuf[SB];
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
     if (!full) {
