@@ -133,19 +133,30 @@ struct Resolved {
 
 // Automatic split count.  Parallel units of the non-split grid are
 // (sequence, kv head, query tile); when they cannot fill the device the key
-// range is cut so that about kTargetPerCu workgroups per compute unit exist,
-// each streaming at least kMinChunk keys.  The split sweeps on the pages show
-// time falling steeply until the grid covers the machine and flattening or
-// rising a little past that point; on MI355X the decode kernel (2 resident
-// workgroups per CU) keeps improving until each CU has seen ~8 waves of
-// workgroups, which also evens out sequences of different lengths.
-int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num_cus) {
+// range is cut into splits of at least kMinChunk keys.  The split sweeps on
+// the pages show time falling steeply until the grid covers the machine and
+// flattening or rising past that point.  On MI355X:
+//  * the decode kernel (2 resident workgroups per CU, one 16-row tile) keeps
+//    improving until each CU has seen ~16 workgroups, which also evens out
+//    sequences of different lengths;
+//  * the multi-row (prefill-family) kernels hold a large LDS ring per
+//    workgroup and run fastest with exactly one wave of workgroups: splits
+//    are chosen so that units x splits just fits the CU count, since a
+//    second round of workgroups on a few CUs doubles the time.
+int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num_cus, bool one_round) {
   constexpr int kTargetPerCu = 16;
   constexpr int64_t kMinChunk = 256;
   if (sk_max <= 0) return 1;
-  const int64_t target = (int64_t)kTargetPerCu * num_cus;
-  if (units >= target / 2) return 1;
-  int64_t chunk = (key_work + target - 1) / target;
+  int64_t chunk;
+  if (one_round) {
+    const int64_t s = num_cus / (units > 0 ? units : 1);
+    if (s <= 1) return 1;
+    chunk = (sk_max + s - 1) / s;
+  } else {
+    const int64_t target = (int64_t)kTargetPerCu * num_cus;
+    if (units >= target / 2) return 1;
+    chunk = (key_work + target - 1) / target;
+  }
   if (chunk < kMinChunk) chunk = kMinChunk;
   chunk = (chunk + sb - 1) / sb * sb;
   int64_t s = (sk_max + chunk - 1) / chunk;
@@ -255,7 +266,7 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     S = a->num_kv_splits;
   } else {
     const int64_t key_work = (int64_t)a->num_heads_kv * pl.num_q_tiles * r->total_k;
-    S = auto_splits(units, key_work, r->sk_max, pl.key_block, num_cus);
+    S = auto_splits(units, key_work, r->sk_max, pl.key_block, num_cus, prefill);
   }
   pl.num_splits = S;
   if (S > 1) {

@@ -221,10 +221,12 @@ def test_auto_splits_off_for_prefill():
 
 
 def test_auto_splits_short_prefix_fp8():
-    a = make(dtype=3, sq=70, sk=16384, hq=12, hkv=12, dqk=192, dv=128, splits=0)
-    n = ctypes.c_int32()
-    assert fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n)) == OK
-    assert n.value > 1
+    # multi-row kernel: one round of workgroups, 12 (sequence, head) units
+    for sk in (16384, 11008):
+        a = make(dtype=3, sq=70, sk=sk, hq=12, hkv=12, dqk=192, dv=128, splits=0)
+        n = ctypes.c_int32()
+        assert fmha.lib.fmha_num_splits(ctypes.byref(a), ctypes.byref(n)) == OK
+        assert 16 <= n.value and n.value * 12 <= 256
 
 
 def test_gqa_rows_packed_into_one_tile():
