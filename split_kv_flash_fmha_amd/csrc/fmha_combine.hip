@@ -5,14 +5,16 @@
 //   L = max_s lse_s;  L = -inf -> O = 0, LSE = -inf;
 //   LSE = L + ln sum_s exp(lse_s - L);  O = sum_s exp(lse_s - LSE) O_s.
 //
-// One 256-thread workgroup per (query row, head).  Thread s < S_b loads
-// lse_s, the workgroup reduces max and sum, and each split's weight is
-// computed once into LDS.  The Dv/4 16-byte column chunks x (256 / (Dv/4))
-// split groups then read disjoint partial rows in parallel (no serial chain
-// of dependent loads) and the split groups are summed through LDS.
+// One 256-thread workgroup per (query row, head, group of cw 16-byte column
+// chunks): thread (chunk c, split group g) owns the partial rows of splits
+// g, g + 256/cw, ... of its chunk (at most 16).  Every thread issues its
+// partial-O loads at once, next to the lse loads, so the workgroup waits for
+// one memory round trip; the weights exp(lse_s - LSE) are then formed once in
+// LDS and the split groups are summed through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fmha.h"
 #include "fmha_params.h"
 
 namespace fmha {
@@ -46,6 +48,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+template <int MAXL>
 __global__ __launch_bounds__(kThreads) void fmha_combine_kernel(CombineParams p) {
   __shared__ float w_s[kThreads];
   __shared__ float red[kThreads / 64];
@@ -53,9 +56,16 @@ __global__ __launch_bounds__(kThreads) void fmha_combine_kernel(CombineParams p)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int nchunk = p.dv >> 2;
+  const int cw = p.chunks_per_wg;                        // chunks per workgroup
+  const int ncg = (nchunk + cw - 1) / cw;                // column groups per row
+  const int ngroups = kThreads / cw;                     // split groups
+  int64_t item = blockIdx.x;
+  const int cg = (int)(item % ncg);
+  item /= ncg;
   const int64_t per_b = (int64_t)p.max_seqlen_q * p.hq;
-  const int b = (int)(blockIdx.x / per_b);
-  const int64_t rem = blockIdx.x % per_b;
+  const int b = (int)(item / per_b);
+  const int64_t rem = item % per_b;
   const int i = (int)(rem / p.hq);
   const int h = (int)(rem % p.hq);
 
@@ -73,11 +83,24 @@ __global__ __launch_bounds__(kThreads) void fmha_combine_kernel(CombineParams p)
   const int64_t t = (int64_t)q_off + i;
   const int64_t lse_split_stride = (int64_t)p.hq * p.total_q;
 
-  // split weights: w_s = exp(lse_s - LSE)
+  // issue every load first: this thread's lse and its partial rows
   const float my_lse = tid < nsb ? p.lse_part[(int64_t)tid * lse_split_stride + (int64_t)h * p.total_q + t]
                                  : -INFINITY;
-  float v = wave_max(my_lse);
-  if (lane == 0) red[wave] = v;
+  const int cl = tid % cw, g = tid / cw;
+  const int c = cg * cw + cl;
+  const bool col_ok = c < nchunk && g < ngroups;
+  const int64_t o_split_stride = (int64_t)p.total_q * p.hq * p.dv;
+  const float* op = p.o_part + (t * p.hq + h) * p.dv + 4 * c;
+  f32x4c v[MAXL];
+#pragma unroll
+  for (int k = 0; k < MAXL; ++k) {
+    const int s = g + k * ngroups;
+    v[k] = (col_ok && s < nsb) ? *(const f32x4c*)(op + s * o_split_stride) : f32x4c{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // split weights: w_s = exp(lse_s - LSE)
+  float mx = wave_max(my_lse);
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
   const float L = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
@@ -90,32 +113,27 @@ __global__ __launch_bounds__(kThreads) void fmha_combine_kernel(CombineParams p)
   w_s[tid] = (tid < nsb && total != -INFINITY) ? exp2f((my_lse - total) * kLog2eC) : 0.f;
   __syncthreads();
 
-  // weighted sum: thread = (split group sg, 4-column chunk c)
-  const int nchunk = p.dv >> 2;
-  const int ngroups = kThreads / nchunk;
-  const int c = tid % nchunk, sg = tid / nchunk;
   f32x4c acc = {0.f, 0.f, 0.f, 0.f};
-  if (sg < ngroups) {
-    const int64_t o_split_stride = (int64_t)p.total_q * p.hq * p.dv;
-    const float* op = p.o_part + (t * p.hq + h) * p.dv + 4 * c;
-#pragma unroll 4
-    for (int s = sg; s < nsb; s += ngroups) acc += w_s[s] * *(const f32x4c*)(op + s * o_split_stride);
+#pragma unroll
+  for (int k = 0; k < MAXL; ++k) {
+    const int s = g + k * ngroups;
+    if (s < nsb) acc += w_s[s] * v[k];
   }
   part[tid] = acc;
   __syncthreads();
-  if (tid < nchunk) {
+  if (tid < cw && c < nchunk) {
     f32x4c o = part[tid];
-    for (int g = 1; g < ngroups; ++g) o += part[g * nchunk + tid];
+    for (int gg = 1; gg < ngroups; ++gg) o += part[gg * cw + tid];
     char* orow = p.o + (p.cu_q ? (int64_t)(q_off + i) * p.o_st : (int64_t)b * p.o_sb + (int64_t)i * p.o_st) +
                  (int64_t)h * p.o_sh;
     if (p.out_dtype == DT_F32) {
-      *(f32x4c*)(orow + (int64_t)tid * 16) = o;
+      *(f32x4c*)(orow + (int64_t)c * 16) = o;
     } else {
       u32x2c wv = {pack2(o.x, o.y, p.out_dtype), pack2(o.z, o.w, p.out_dtype)};
-      *(u32x2c*)(orow + (int64_t)tid * 8) = wv;
+      *(u32x2c*)(orow + (int64_t)c * 8) = wv;
     }
   }
-  if (p.lse && tid == 0) {
+  if (p.lse && tid == 0 && cg == 0) {
     const int64_t li = p.cu_q ? (int64_t)h * p.lse_sh + q_off + i : (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i;
     p.lse[li] = total;
   }
@@ -124,9 +142,23 @@ __global__ __launch_bounds__(kThreads) void fmha_combine_kernel(CombineParams p)
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  const int64_t items = (int64_t)p.max_seqlen_q * p.hq * p.batch;
+  const int cw = p.chunks_per_wg, nchunk = p.dv / 4;
+  if (cw <= 0) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)p.max_seqlen_q * p.hq * p.batch * ((nchunk + cw - 1) / cw);
   if (items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fmha_combine_kernel, dim3((uint32_t)items), dim3(kThreads), 0, stream, p);
+  const int loads = (p.num_splits + kThreads / cw - 1) / (kThreads / cw);
+  const dim3 grid((uint32_t)items), block(kThreads);
+  if (loads <= 2) {
+    hipLaunchKernelGGL(fmha_combine_kernel<2>, grid, block, 0, stream, p);
+  } else if (loads <= 4) {
+    hipLaunchKernelGGL(fmha_combine_kernel<4>, grid, block, 0, stream, p);
+  } else if (loads <= 8) {
+    hipLaunchKernelGGL(fmha_combine_kernel<8>, grid, block, 0, stream, p);
+  } else if (loads <= 16) {
+    hipLaunchKernelGGL(fmha_combine_kernel<16>, grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

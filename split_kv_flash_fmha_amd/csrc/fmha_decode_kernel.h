@@ -15,7 +15,10 @@
 //    transpose reads (ds_read_b64_tr_b16 / _b8) as the A operand of
 //    O^T += V^T P^T.
 //  * The next 32-key block's K and V are in flight (registers) while the
-//    current block is computed.
+//    current block is computed.  Every K and V byte is read exactly once, so
+//    the loads are non-temporal (streamed past the caches instead of
+//    displacing other lines).  The rows are whole and contiguous per load,
+//    so no line is fetched twice.
 //  * The NW waves' (m, l, O) are merged through LDS; the result is written as
 //    the final row (no split) or as this split's fp32 partial.
 //
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_decode_kernel(FwdParams p) {
 #pragma unroll
       for (int c = 0; c < C::CQK; ++c) {
         u32x4 z = {0u, 0u, 0u, 0u};
-        kr[u][c] = ok ? *(const u32x4*)(src + (4 * c + lg) * 16) : z;
+        kr[u][c] = ok ? __builtin_nontemporal_load((const u32x4*)(src + (4 * c + lg) * 16)) : z;
       }
     }
 #pragma unroll
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_decode_kernel(FwdParams p) {
       const int key = flat / (C::VROW / 16), part = flat % (C::VROW / 16);
       const int j = j0 + key;
       u32x4 z = {0u, 0u, 0u, 0u};
-      vr[n] = j < w_hi ? *(const u32x4*)(vbase + (int64_t)j * p.v_st + part * 16) : z;
+      vr[n] = j < w_hi ? __builtin_nontemporal_load((const u32x4*)(vbase + (int64_t)j * p.v_st + part * 16)) : z;
     }
   };
 

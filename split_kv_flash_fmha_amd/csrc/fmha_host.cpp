@@ -284,7 +284,7 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   }
   pl.grid_main = r->empty ? 0 : (int64_t)S * units;
   if (pl.grid_main >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
-  pl.grid_combine = (r->empty || S == 1) ? 0 : r->sq_max * a->num_heads_q * a->batch;
+  pl.grid_combine = (r->empty || S == 1) ? 0 : combine_grid(a->head_dim_v, S, r->sq_max * a->num_heads_q * a->batch);
   if (pl.grid_combine >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
   if (mode != kQuery && S > 1 && !r->empty) {
     if (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < pl.workspace_bytes)
@@ -363,6 +363,7 @@ CombineParams make_combine(const fmha_fwd_args* a, const Resolved& r) {
   c.dv = a->head_dim_v;
   c.num_splits = r.plan.num_splits;
   c.chunk = r.plan.split_chunk;
+  c.chunks_per_wg = combine_chunks_per_wg(a->head_dim_v, c.num_splits, r.sq_max * a->num_heads_q * a->batch);
   c.o_sb = a->o_stride_batch * ob;
   c.o_st = a->o_stride_tok * ob;
   c.o_sh = a->o_stride_head * ob;
@@ -444,7 +445,7 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
   if (!a) return FMHA_ERR_INVALID_ARG;
   const int ob = elem_bytes(a->out_dtype);
   if (ob == 0 || a->out_dtype == FMHA_DTYPE_FP8_E4M3) return FMHA_ERR_INVALID_ARG;
-  // the combine moves 4 consecutive Dv elements per thread, one workgroup per row
+  // the combine moves 4 consecutive Dv elements per thread
   if (a->batch < 0 || a->num_heads_q <= 0 || a->head_dim_v <= 0 || a->head_dim_v % 4 ||
       a->head_dim_v > 1024)
     return FMHA_ERR_INVALID_ARG;
@@ -461,7 +462,7 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
   if (a->o_stride_tok < 0 || a->o_stride_head < 0 || a->o_stride_tok % 4 || a->o_stride_head % 4 ||
       (!vq && (a->o_stride_batch < 0 || a->o_stride_batch % 4)))
     return FMHA_ERR_INVALID_ARG;
-  if (sq_max * a->num_heads_q * a->batch >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
+  if (combine_grid(a->head_dim_v, a->num_splits, sq_max * a->num_heads_q * a->batch) >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
   CombineParams c;
   memset(&c, 0, sizeof(c));
   c.o_part = a->o_part;
@@ -479,6 +480,7 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
   c.dv = a->head_dim_v;
   c.num_splits = a->num_splits;
   c.chunk = a->split_chunk;
+  c.chunks_per_wg = combine_chunks_per_wg(a->head_dim_v, a->num_splits, sq_max * a->num_heads_q * a->batch);
   c.o_sb = a->o_stride_batch * ob;
   c.o_st = a->o_stride_tok * ob;
   c.o_sh = a->o_stride_head * ob;

@@ -52,6 +52,7 @@ struct CombineParams {
   int32_t batch, seqlen_q, seqlen_k, max_seqlen_q, total_q;
   int32_t hq, dv;
   int32_t num_splits, chunk;
+  int32_t chunks_per_wg;     // combine_chunks_per_wg()
   int64_t o_sb, o_st, o_sh;  // bytes
   int64_t lse_sb, lse_sh;    // elements
   int32_t out_dtype;
@@ -86,6 +87,25 @@ const FwdKernel* registry_f32_prefill(int* n);
 const FwdKernel* registry_f16_prefill(int* n);
 const FwdKernel* registry_bf16_prefill(int* n);
 const FwdKernel* registry_fp8_prefill(int* n);
+
+// Shape of the combine grid: a workgroup (256 threads) takes cw of a row's
+// Dv / 4 16-byte column chunks (cw a power of two) and 256 / cw split groups.
+// Few rows get narrow column groups (more workgroups in flight); cw is also
+// kept small enough that no thread owns more than 16 partial rows.
+constexpr int kCombineMaxChunks = 32;   // widest column group (chunks)
+constexpr int64_t kCombineMinWgs = 128; // narrower groups until the grid has this many
+inline int combine_chunks_per_wg(int dv, int num_splits, int64_t rows) {
+  const int nchunk = dv / 4;
+  int cw = 1;
+  while (cw < nchunk && cw < kCombineMaxChunks) cw *= 2;
+  while (cw > 4 && rows * ((nchunk + cw - 1) / cw) < kCombineMinWgs) cw /= 2;
+  while (cw > 1 && (num_splits + 256 / cw - 1) / (256 / cw) > 16) cw /= 2;
+  return cw;
+}
+inline int64_t combine_grid(int dv, int num_splits, int64_t rows) {
+  const int nchunk = dv / 4, cw = combine_chunks_per_wg(dv, num_splits, rows);
+  return rows * ((nchunk + cw - 1) / cw);
+}
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
