@@ -110,9 +110,8 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_decode_kernel(FwdParams p) {
   float scale_log2 = p.scale_log2;
   float v_scale = 1.0f;
   if constexpr (DT == DT_FP8) {
-    if (p.q_descale) scale_log2 *= *p.q_descale;
-    if (p.k_descale) scale_log2 *= *p.k_descale;
-    if (p.v_descale) v_scale = *p.v_descale;
+    scale_log2 *= load_scale(p.q_descale, p.q) * load_scale(p.k_descale, p.q);
+    v_scale = load_scale(p.v_descale, p.q);
     v_scale *= 1.0f / kFp8PScale;
   }
 

@@ -44,7 +44,7 @@ const FwdKernel* registry_fp8_decode(int* n) {
 // 32x32-tile fp8 instances (32 rows per wave, 64-key blocks); nwm picked by
 // rows per (sequence, kv head).
 #define FMHA_PF8(DQK, DV, NWM, ID) \
-  {DT_FP8, DQK, DV, NWM, 1, 64, ID, &launch_prefill8<Pf8Cfg<DQK, DV, NWM>>}
+  {DT_FP8, DQK, DV, NWM, 1, 64, ID, &launch_prefill8<Pf8Cfg<DQK, DV, NWM, 1>>}
 
 static const FwdKernel kPf8Table[] = {
     FMHA_PF8(192, 128, 3, 210),

@@ -172,6 +172,15 @@ __device__ __forceinline__ WorkItem work_item(const FwdParams& p) {
   return w;
 }
 
+// Per-tensor fp8 scale: *ptr, or 1 when ptr is null.  The load is made
+// unconditionally (from `fallback`, any readable 4-byte-aligned address, when
+// ptr is null) so a kernel's scale loads are issued together and waited for
+// once, instead of one dependent round trip each behind a branch.
+__device__ __forceinline__ float load_scale(const float* ptr, const void* fallback) {
+  const float v = *(ptr ? ptr : (const float*)fallback);
+  return ptr ? v : 1.0f;
+}
+
 __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
@@ -285,9 +294,8 @@ __global__ __launch_bounds__(C::NTHR) void fmha_fwd_kernel(FwdParams p) {
   float scale_log2 = p.scale_log2;
   float v_scale = 1.0f;
   if constexpr (DT == DT_FP8) {
-    if (p.q_descale) scale_log2 *= *p.q_descale;
-    if (p.k_descale) scale_log2 *= *p.k_descale;
-    if (p.v_descale) v_scale = *p.v_descale;
+    scale_log2 *= load_scale(p.q_descale, p.q) * load_scale(p.k_descale, p.q);
+    v_scale = load_scale(p.v_descale, p.q);
     v_scale *= 1.0f / kFp8PScale;
   }
 

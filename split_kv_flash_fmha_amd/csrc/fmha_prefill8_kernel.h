@@ -24,8 +24,8 @@
 //    factor 8 is carried by l as well (it cancels in O and is taken out of the
 //    LSE); a row's 32 stored values sum to at most 448 unless the check sends
 //    the block to the slow path, so each stays inside e4m3's range.
-//  * Rings of four K stages and three V stages in LDS; K runs three blocks and
-//    V two blocks ahead of use.
+//  * Rings of LA + 2 K and V stages in LDS: the loads of LA key blocks are in
+//    flight while a block is computed.
 #pragma once
 #include "fmha_prefill_kernel.h"
 
@@ -46,7 +46,7 @@ __device__ __forceinline__ f32x16 mfma64_fp8(f32x16 acc, u32x8 a, u32x8 b) {
                                                          acc, 0, 0, 0, 0, 0, 0);
 }
 
-template <int DQK_, int DV_, int NWM_>
+template <int DQK_, int DV_, int NWM_, int LA_>
 struct Pf8Cfg {
   static constexpr int DQK = DQK_;
   static constexpr int DV = DV_;
@@ -58,19 +58,20 @@ struct Pf8Cfg {
   static constexpr int NT = BN / 32;
   static constexpr int TV = DV / 32;
   static constexpr int NG = 2 * NT;      // PV groups of 16 keys
-  static constexpr int KCOLS = DQK / 16;
-  static constexpr int VCOLS = DV / 16;
-  static constexpr int KCP = BN * 16;        // K column pitch
-  static constexpr int VCP = BN * 16 + 64;   // V column pitch
-  static constexpr int KTILE = KCOLS * KCP;
-  static constexpr int VTILE = VCOLS * VCP;
-  static constexpr int NSK = 4;                         // K ring stages
-  static constexpr int NSV = 3;                         // V ring stages
-  static constexpr int KL = (KCOLS + NWM - 1) / NWM;    // K column loads per wave per block
-  static constexpr int VL = (VCOLS + NWM - 1) / NWM;    // V column loads per wave per block
+  static constexpr int KPITCH = DQK + 16;   // K row pitch in LDS: one 16-byte pad slot per row
+  static constexpr int KSLOTS = KPITCH / 16;
+  static constexpr int KTILE = BN * KPITCH;
+  static constexpr int VTILE = BN * DV;      // V rows unpadded, 16-byte chunks XOR-swizzled
+  static constexpr int KLD = KTILE / 1024;   // 1 KiB buffer->LDS loads per K block
+  static constexpr int VLD = VTILE / 1024;
+  static constexpr int LA = LA_;                        // key blocks of loads in flight
+  static constexpr int NSK = LA + 2;                    // K ring stages
+  static constexpr int NSV = LA + 2;                    // V ring stages
+  static constexpr int KL = (KLD + NWM - 1) / NWM;      // K loads per wave per block
+  static constexpr int VL = (VLD + NWM - 1) / NWM;      // V loads per wave per block
   static constexpr int LDS = NSK * KTILE + NSV * VTILE;
-  static_assert(DQK % 64 == 0 && DV % 32 == 0, "head dims");
-  static_assert(KTILE % 256 == 0 && VTILE % 64 == 0, "stage offsets");
+  static_assert(DQK % 64 == 0 && DV == 128, "head dims (the V swizzle assumes 8 chunks per row)");
+  static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "whole 1 KiB loads per tile");
 };
 
 template <class C>
@@ -119,11 +120,12 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   const int hq = hkv * G + (row_ok ? r % G : 0);
 
   float scale_log2 = p.scale_log2;
-  if (p.q_descale) scale_log2 *= *p.q_descale;
-  if (p.k_descale) scale_log2 *= *p.k_descale;
-  const float v_scale = p.v_descale ? *p.v_descale : 1.0f;
+  scale_log2 *= load_scale(p.q_descale, p.q) * load_scale(p.k_descale, p.q);
+  const float v_scale = load_scale(p.v_descale, p.q);
 
   // Q^T (B operand): d chunk c, lane half h holds Q bytes [64c + 32h, +32)
+  // (a lane past the tile's rows reads row 0's Q: its results are never stored,
+  // and leaving its Q unmasked keeps the prologue from waiting on the Q loads)
   u32x8 qf[C::KC];
   {
     const char* qrow = p.q + (p.cu_q ? (int64_t)(q_off + iq) * p.q_st : (int64_t)b * p.q_sb + (int64_t)iq * p.q_st) +
@@ -133,7 +135,6 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
       const u32x4 lo = *(const u32x4*)(qrow + 64 * c + 32 * hl);
       const u32x4 hi = *(const u32x4*)(qrow + 64 * c + 32 * hl + 16);
       qf[c] = u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (!row_ok) qf[c] = u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     }
   }
 
@@ -160,45 +161,67 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // per-lane parts of the LDS read addresses (stage offsets added per block)
+  // LDS layout of a key block (64 rows):
+  //  * K row r at r * KPITCH, chunk c at 16c (slot KSLOTS-1 is padding): the
+  //    16-byte reads of 16 consecutive rows at one chunk hit distinct banks.
+  //  * V row r at r * 128, chunk c at slot c ^ vswz(r), vswz(r) =
+  //    2 * bit1(r) + 4 * bit3(r): the eight 32-byte row pieces a 32-lane
+  //    transpose-read pass touches (rows {0..3, 8..11} + 4h) hit distinct banks.
+  // Per-lane parts of the read addresses (stage offsets added per block).
   const uint32_t lds0 = lds_addr(smem);
-  const uint32_t k_rd = lds0 + (uint32_t)(2 * hl * C::KCP + lr * 16);  // + 4c*KCP (+KCP) + 32u*16
+  const uint32_t k_rd = lds0 + (uint32_t)(lr * C::KPITCH + 32 * hl);  // + 32u*KPITCH + 64c (+16)
   const int gq = (lane >> 4) & 1, i16 = lane & 15, e8 = i16 >> 1, jh = i16 & 1;
-  const uint32_t v_rd = lds0 + (uint32_t)(C::NSK * C::KTILE + gq * C::VCP +
-                                          (8 * (e8 >> 2) + 4 * hl + (e8 & 3)) * 16 + 8 * jh);  // + 2t*VCP + (32u+16m)*16
+  const int vswz_e = 2 * ((e8 >> 1) & 1) + 4 * ((e8 >> 2) & 1);  // vswz of this lane's rows
+  uint32_t v_rd[C::TV];  // dv tile t: + (32u+16m)*128
+#pragma unroll
+  for (int t = 0; t < C::TV; ++t)
+    v_rd[t] = lds0 + (uint32_t)(C::NSK * C::KTILE + (8 * (e8 >> 2) + 4 * hl + (e8 & 3)) * C::DV +
+                                16 * ((2 * t + gq) ^ vswz_e) + 8 * jh);
 
-  // zero the LDS once so no slot is read uninitialised
-  for (int i = tid * 16; i < C::LDS; i += C::NTHR * 16) *(u32x4*)(smem + i) = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  // No LDS initialisation: every slot a read touches is written by a load
+  // first (rows past a block's end and empty blocks are loaded as zeros; K pad
+  // slots are never read), so the prologue's K/V loads go out at once.
 
-  // One 1 KiB load = 16-byte column c of the 64 rows of a block (lane = row).
-  // The descriptor covers the rows of the block the tile needs (rows past them
-  // read as zero; a block past them gets an empty descriptor and fetches
-  // nothing).  Every wave issues exactly KL K and VL V loads per block (the
-  // last column repeated where the columns do not divide evenly; identical
+  // One 1 KiB load fills LDS bytes [1024 i, 1024 i + 1024) of a tile; lane l
+  // writes 16-byte slot 64 i + l and fetches the row chunk the layout puts
+  // there, so the 64 lanes read whole rows (5.3 K rows or 8 V rows) from
+  // HBM.  K pad slots take an offset past the descriptor (read as zero, no
+  // fetch).  The descriptor covers the rows of the block the tile needs (rows
+  // past them read as zero; a block past them gets an empty descriptor and
+  // fetches nothing).  Every wave issues exactly KL K and VL V loads per block
+  // (the last load repeated where the loads do not divide evenly; identical
   // bytes), so the loads a wave has in flight are a compile-time count.
   auto block_rsrc = [&](const char* base, int64_t st, int jb, int rowb) {
     const int rows_left = min(j_end - jb, C::BN);
     const int nb = rows_left > 0 ? (rows_left - 1) * (int)st + rowb : 0;
     return make_rsrc(base + (int64_t)jb * st, nb);
   };
+  int k_src[C::KL], k_dst[C::KL], v_src[C::VL], v_dst[C::VL];
+#pragma unroll
+  for (int n = 0; n < C::KL; ++n) {
+    const int i = min(wm + n * C::NWM, C::KLD - 1);
+    const int slot = 64 * i + lane, r = slot / C::KSLOTS, c = slot % C::KSLOTS;
+    k_src[n] = c < C::DQK / 16 ? r * (int)p.k_st + 16 * c : 0x7ffffff0;
+    k_dst[n] = 1024 * i;
+  }
+#pragma unroll
+  for (int n = 0; n < C::VL; ++n) {
+    const int i = min(wm + n * C::NWM, C::VLD - 1);
+    const int r = 8 * i + (lane >> 3), c = (lane & 7) ^ (2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1));
+    v_src[n] = r * (int)p.v_st + 16 * c;
+    v_dst[n] = 1024 * i;
+  }
   auto issue_k = [&](int jb, int st) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, p.k_st, jb, C::DQK);
     char* dst = smem + st * C::KTILE;
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      const int c = min(wm + i * C::NWM, C::KCOLS - 1);
-      buffer_to_lds16(rk, dst + c * C::KCP, lane * (int)p.k_st + c * 16);
-    }
+    for (int n = 0; n < C::KL; ++n) buffer_to_lds16(rk, dst + k_dst[n], k_src[n]);
   };
   auto issue_v = [&](int jb, int st) {
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, p.v_st, jb, C::DV);
     char* dst = smem + C::NSK * C::KTILE + st * C::VTILE;
 #pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      const int c = min(wm + i * C::NWM, C::VCOLS - 1);
-      buffer_to_lds16(rv, dst + c * C::VCP, lane * (int)p.v_st + c * 16);
-    }
+    for (int n = 0; n < C::VL; ++n) buffer_to_lds16(rv, dst + v_dst[n], v_src[n]);
   };
   auto wait_loads = [](auto N_) {
     constexpr int n = decltype(N_)::value;
@@ -213,18 +236,18 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   // O^T += V^T P^T from V stage vst: MFMA t (dv tile t) takes V^T from four
   // transpose reads, read (t, g) for key group g = (u, m): lane 2e+jh of
   // 16-lane group (hl, gq) reads key row 32u+16m+8(e/4)+4hl+e%4, dv bytes
-  // 32t+16gq+8jh..+7, and receives dv column lr of those 8 keys (bytes 8g..8g+7
-  // of its operand).  Reads run two MFMAs ahead; `between(t)` is VALU work
+  // 32t+16gq+8jh..+7 (at the row's swizzled chunk slot), and receives dv
+  // column lr of those 8 keys (bytes 8g..8g+7 of its operand).  Reads run two MFMAs ahead; `between(t)` is VALU work
   // after MFMA t.
   auto pv = [&](int vst, const u32x8& pb, auto&& between) {
     constexpr int NM = C::TV;
-    const uint32_t vb = v_rd + (uint32_t)(vst * C::VTILE);
+    const uint32_t vso = (uint32_t)(vst * C::VTILE);
     i32x2 vr[3][4];
     auto read_frag = [&](auto T_) {
       constexpr int t = decltype(T_)::value;
       static_for<4>([&](auto G_) {
         constexpr int g = decltype(G_)::value, u = g >> 1, m = g & 1;
-        vr[t % 3][g] = lds_tr8<2 * t * C::VCP + (32 * u + 16 * m) * 16>(vb);
+        vr[t % 3][g] = lds_tr8<(32 * u + 16 * m) * C::DV>(v_rd[t] + vso);
       });
     };
     read_frag(int_c<0>{});
@@ -257,8 +280,8 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     u32x4 kf[3][2];
     auto read_k = [&](auto N_) {
       constexpr int n = decltype(N_)::value, u = n / C::KC, c = n % C::KC;
-      kf[n % 3][0] = lds_b128<4 * c * C::KCP + 32 * u * 16>(kbs);
-      kf[n % 3][1] = lds_b128<(4 * c + 1) * C::KCP + 32 * u * 16>(kbs);
+      kf[n % 3][0] = lds_b128<32 * u * C::KPITCH + 64 * c>(kbs);
+      kf[n % 3][1] = lds_b128<32 * u * C::KPITCH + 64 * c + 16>(kbs);
     };
     read_k(int_c<0>{});
     if constexpr (NM > 1) read_k(int_c<1>{});
@@ -307,39 +330,44 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   };
   auto words_upto = [](int k) { return (k * NWD) / (NPV + NQK); };
 
-  // Rings: K(b) in K stage b % 4, V(b) in V stage b % 3.  Iteration it issues
-  // K(it+4) and V(it+1) and needs K(it+1) (QK) and V(it-1) (PV): only the
-  // previous iteration's loads may still be in flight.  The prologue issues in
-  // the order iterations -4..-1 would (empty loads for V(-3)..V(-1)).
+  // Rings of NS = LA + 2 stages: K(b) in K stage b % NS, V(b) in V stage
+  // b % NS.  Iteration it issues K(it+NS) and V(it+LA) and needs K(it+1) (QK)
+  // and V(it-1) (PV), issued NS-1 and LA+1 iterations earlier: the loads of
+  // the last LA iterations may still be in flight.  The prologue issues in
+  // the order iterations -NS..-1 would (empty loads for V(<0); they land
+  // before any real load of the same stage, loads completing in order).
+  constexpr int NS = C::NSK;
+  static_assert(C::NSV == NS, "one ring depth");
   f32x16 sbuf[2][C::NT];
   const int jlast = j_begin + n_iter * C::BN;
   if (n_iter > 0) {
-    issue_k(j_begin, 0);
-    issue_v(jlast, 1);  // empty
-    issue_k(j_begin + C::BN, 1);
-    issue_v(jlast, 1);  // empty
-    issue_k(j_begin + 2 * C::BN, 2);
-    issue_v(jlast, 1);  // empty
-    issue_k(j_begin + 3 * C::BN, 3);
-    issue_v(j_begin, 0);
-    wait_loads(int_c<3 * C::KL + 4 * C::VL>{});  // K(0) landed
+    static_for<NS>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;  // iteration i - NS
+      issue_k(j_begin + i * C::BN, i);
+      constexpr int vb = i - NS + C::LA;      // V block of that iteration
+      if constexpr (vb >= 0)
+        issue_v(j_begin + vb * C::BN, vb);
+      else
+        issue_v(jlast, NS - 1);  // empty
+    });
+    wait_loads(int_c<(NS - 1) * (C::KL + C::VL) + C::VL>{});  // K(0) landed
     block_barrier();
     qk(0, sbuf[0], nothing);
   }
 
-  int kst = 1;  // (it + 1) % 4: K stage of QK(it+1)
-  int vst = 2;  // (it - 1) % 3: V stage of PV(it-1)
+  int kst = 1;       // (it + 1) % NS: K stage of QK(it+1)
+  int vst = NS - 1;  // (it - 1) % NS: V stage of PV(it-1)
   // SB = it % 2 at compile time (S and P buffers stay in registers)
   auto body = [&](auto SB_, auto FIRST_, int it) {
     constexpr int SB = decltype(SB_)::value;
     constexpr bool FIRST = decltype(FIRST_)::value != 0;
     const int j0 = j_begin + it * C::BN;
-    wait_loads(int_c<C::KL + C::VL>{});
-    block_barrier();  // K(it+1), V(it-1) in LDS everywhere; K stage it%4, V stage (it+1)%3 free
-    const int kst_free = kst == 0 ? 3 : kst - 1;  // it % 4
-    const int vst_free = vst == 0 ? 2 : vst - 1;              // (it + 1) % 3 == (vst + 2) % 3
-    issue_k(j0 + 4 * C::BN, kst_free);
-    issue_v(j0 + C::BN, vst_free);
+    wait_loads(int_c<C::LA * (C::KL + C::VL)>{});
+    block_barrier();  // K(it+1), V(it-1) in LDS everywhere; K stage it%NS, V stage (it-2)%NS free
+    const int kst_free = kst == 0 ? NS - 1 : kst - 1;  // it % NS
+    const int vst_free = vst == 0 ? NS - 1 : vst - 1;  // (it + LA) % NS == (it - 2) % NS
+    issue_k(j0 + NS * C::BN, kst_free);
+    issue_v(j0 + C::LA * C::BN, vst_free);
     f32x16 (&s)[C::NT] = sbuf[SB];
     u32x8& pc = pbuf[SB];
 
@@ -391,8 +419,8 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
       static_for<NWD>([&](auto W_) { exp_word(s, pc, nb2, rs, W_); });
     }
     l_run += rs;
-    kst = kst == 3 ? 0 : kst + 1;
-    vst = vst == 2 ? 0 : vst + 1;
+    kst = kst == NS - 1 ? 0 : kst + 1;
+    vst = vst == NS - 1 ? 0 : vst + 1;
   };
 
   if (n_iter > 0) {
@@ -402,7 +430,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
       if (++it >= n_iter) break;
       body(int_c<0>{}, int_c<0>{}, it);
     }
-    // PV of the last block (V stage (n_iter-1) % 3 == vst, P of block n_iter-1)
+    // PV of the last block (V stage (n_iter-1) % NS == vst, P of block n_iter-1)
     __builtin_amdgcn_s_waitcnt(0);
     block_barrier();
     if ((n_iter - 1) & 1)

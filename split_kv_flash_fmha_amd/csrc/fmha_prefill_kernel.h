@@ -333,7 +333,12 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   // zero the LDS once so no slot is ever read uninitialised
 #pragma unroll
   for (int i = tid * 16; i < C::LDS; i += C::NTHR * 16) *(u32x4*)(smem + i) = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  // The zero stores must land before any buffer->LDS load of another wave
+  // does: wait for them (lgkmcnt), then a bare barrier.  __syncthreads()
+  // would also wait for the Q loads in flight (vmcnt(0)), putting their
+  // latency in front of the first K/V loads.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  block_barrier();
 
   // descriptor of key block jb: rows [jb, min(jb + BN, j_end)) of K or V
   auto block_rsrc = [&](const char* base, int64_t st, int jb) {
