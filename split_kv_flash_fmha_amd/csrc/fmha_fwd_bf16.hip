@@ -50,7 +50,7 @@ const FwdKernel* registry_bf16_decode(int* n) {
 // workgroups share a CU, so the two waves on a SIMD belong to different
 // workgroups and drift out of phase (one on MFMA while the other is on VALU).
 #define FMHA_PF(D, NWM, BN, ID) \
-  {DT_BF16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_BF16, D, NWM, BN>>}
+  {DT_BF16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_BF16, D, NWM, BN, 1>>}
 
 static const FwdKernel kPfTable[] = {
     FMHA_PF(64, 4, 64, 200),

@@ -50,7 +50,12 @@ const FwdKernel* registry_f16_decode(int* n) {
 // workgroups share a CU, so the two waves on a SIMD belong to different
 // workgroups and drift out of phase (one on MFMA while the other is on VALU).
 #define FMHA_PF(D, NWM, BN, ID) \
-  {DT_F16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, NWM, BN>>}
+  {DT_F16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, NWM, BN, 1>>}
+
+// RT = 2: two waves x 64 rows (two 32-row tiles per wave: every K / V
+// fragment read from LDS feeds two MFMAs); `nwm` counts 32-row tiles.
+#define FMHA_PF2(D, NWM, BN, ID) \
+  {DT_F16, D, D, 2 * NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, NWM, BN, 2>>}
 
 static const FwdKernel kPfTable[] = {
     FMHA_PF(64, 4, 64, 200),

@@ -143,10 +143,12 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   auto hi_of = [&](int i) { return p.wr >= 0 ? min(i + shift + p.wr, sk - 1) : sk - 1; };
   const int last_row = min(row0 + C::ROWS, rows) - 1;
   const int iq_lo = row0 / G, iq_hi = last_row / G;
-  const int tile_lo = max(kb, lo_of(iq_lo));
-  const int tile_hi = min(ke - 1, hi_of(iq_hi));
-  const int full_lo = max(kb, lo_of(iq_hi));
-  const int full_hi = min(ke - 1, hi_of(iq_lo));
+  // the tile's key ranges are uniform; readfirstlane keeps them (and the
+  // buffer descriptors built from them) in scalar registers
+  const int tile_lo = __builtin_amdgcn_readfirstlane(max(kb, lo_of(iq_lo)));
+  const int tile_hi = __builtin_amdgcn_readfirstlane(min(ke - 1, hi_of(iq_hi)));
+  const int full_lo = __builtin_amdgcn_readfirstlane(max(kb, lo_of(iq_hi)));
+  const int full_hi = __builtin_amdgcn_readfirstlane(min(ke - 1, hi_of(iq_lo)));
   const int my_lo = max(kb, lo_of(iq));
   const int my_hi = min(ke - 1, hi_of(iq));
   const int j_begin = (tile_lo / C::BN) * C::BN;

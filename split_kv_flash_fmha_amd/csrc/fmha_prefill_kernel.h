@@ -71,14 +71,15 @@ __device__ __forceinline__ uint32_t pack2_p(float a, float b) {
   }
 }
 
-template <int DT_, int D_, int NWM_, int BN_>
+template <int DT_, int D_, int NWM_, int BN_, int RT_>
 struct PfCfg {
   static constexpr int DT = DT_;
   static constexpr int D = D_;          // Dqk == Dv
-  static constexpr int NWM = NWM_;      // waves, 32 rows each
+  static constexpr int NWM = NWM_;      // waves
+  static constexpr int RT = RT_;        // 32-row tiles per wave (each K/V fragment feeds RT MFMAs)
   static constexpr int BN = BN_;        // keys per block
   static constexpr int NTHR = 64 * NWM;
-  static constexpr int ROWS = 32 * NWM;
+  static constexpr int ROWS = 32 * NWM * RT;
   static constexpr int KS = D / 16;     // k-steps of QK (16 d each)
   static constexpr int NT = BN / 32;    // S^T tiles (32 keys each)
   static constexpr int TV = D / 32;     // O^T tiles (32 dv each)
@@ -89,7 +90,7 @@ struct PfCfg {
   static constexpr int KL = TILE / 1024 / NWM;     // 1 KiB loads per wave per K (or V) block
   static constexpr int NS = 4;                     // ring depth, K and V each
   static constexpr int LDS = 2 * NS * TILE;
-  static constexpr int MIN_BLOCKS = 8 / NWM;       // two waves per SIMD
+  static constexpr int MIN_BLOCKS = (RT == 1 ? 8 : 4) / NWM;  // two waves per SIMD (one for RT = 2)
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
   static_assert(1024 % ROWB == 0 && KL >= 1 && KL * NWM * 1024 == TILE, "whole 1 KiB loads per wave");
   static_assert(TILE % 256 == 0, "stage offsets keep the low address bits");
@@ -210,9 +211,19 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Read schedule of the interleaved PV/QK phase: reads are numbered in the
+// order MFMA j = 0, 1, ... (PV n = j / 2 for even j, QK n for odd j) needs
+// them, three per fragment pair (two V transpose reads, one K read).
+constexpr int kPvqkAhead = 9;  // reads issued beyond the ones the next MFMA needs
+// reads that must have completed before MFMA j
+constexpr int pvqk_need(int j) { return 3 * (j / 2) + (j % 2 ? 3 : 2); }
+// reads issued before MFMA j
+constexpr int pvqk_issued(int j, int nr) { return pvqk_need(j) + kPvqkAhead < nr ? pvqk_need(j) + kPvqkAhead : nr; }
+
 template <class C>
 __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(FwdParams p) {
   constexpr int DT = C::DT;
+  constexpr int RT = C::RT;
   // 256-byte alignment: stage offsets and the XOR swizzles compose by addition
   __shared__ __attribute__((aligned(256))) char smem[C::LDS];
 
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   const int lane = tid & 63;
   const int wm = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int hl = lane >> 5;   // lane half: contraction slots / output row group
-  const int lr = lane & 31;   // query row within the wave / MFMA column
+  const int lr = lane & 31;   // query row within a 32-row tile / MFMA column
 
   const WorkItem wi = work_item(p);
   const int S = p.num_splits;
@@ -244,29 +255,36 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   const int G = p.group;
   const int rows = sq * G;
   const int row0 = qtile * C::ROWS;
-  if (row0 >= rows || sk <= 0) return;
+  if (row0 >= rows || sk <= 0) return;  // past the sequence or no keys: rows untouched
   const int kb = split * p.chunk;
-  if (kb >= sk) return;
+  if (kb >= sk) return;                 // split beyond this sequence: not read by the combine
   const int ke = S > 1 ? min(kb + p.chunk, sk) : sk;
 
+  // ---- pointers
   const char* kbase = p.k + (p.cu_k ? (int64_t)k_off * p.k_st : (int64_t)b * p.k_sb) + (int64_t)hkv * p.k_sh;
   const char* vbase = p.v + (p.cu_k ? (int64_t)k_off * p.v_st : (int64_t)b * p.v_sb) + (int64_t)hkv * p.v_sh;
 
-  const int r = row0 + 32 * wm + lr;
-  const bool row_ok = r < rows;
-  const int iq = row_ok ? r / G : 0;
-  const int hq = hkv * G + (row_ok ? r % G : 0);
-
-  // Q^T (B operand): k-step s, lane half h holds d = 16s + 8h .. +8
-  u32x4 qf[C::KS];
-  {
-    const char* qrow = p.q + (p.cu_q ? (int64_t)(q_off + iq) * p.q_st : (int64_t)b * p.q_sb + (int64_t)iq * p.q_st) +
-                       (int64_t)hq * p.q_sh;
+  // ---- this lane's query rows: one per 32-row tile rt of the wave
+  int iq[RT], hq[RT];
+  bool row_ok[RT];
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qf[s] = row_ok ? *(const u32x4*)(qrow + (16 * s + 8 * hl) * 2) : z;
-    }
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = row0 + 32 * (RT * wm + rt) + lr;
+    row_ok[rt] = r < rows;
+    iq[rt] = row_ok[rt] ? r / G : 0;
+    hq[rt] = hkv * G + (row_ok[rt] ? r % G : 0);
+  }
+
+  // Q^T (B operand): k-step s, lane half h holds d = 16s + 8h .. +8.  A lane
+  // past the tile's rows reads row 0's Q: its results are never stored, and
+  // leaving its Q unmasked keeps the prologue from waiting on the Q loads.
+  u32x4 qf[RT][C::KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const char* qrow = p.q + (p.cu_q ? (int64_t)(q_off + iq[rt]) * p.q_st : (int64_t)b * p.q_sb + (int64_t)iq[rt] * p.q_st) +
+                       (int64_t)hq[rt] * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) qf[rt][s] = *(const u32x4*)(qrow + (16 * s + 8 * hl) * 2);
   }
   const float scale_log2 = p.scale_log2;
 
@@ -275,23 +293,35 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   auto hi_of = [&](int i) { return p.wr >= 0 ? min(i + shift + p.wr, sk - 1) : sk - 1; };
   const int last_row = min(row0 + C::ROWS, rows) - 1;
   const int iq_lo = row0 / G, iq_hi = last_row / G;
-  const int tile_lo = max(kb, lo_of(iq_lo));
-  const int tile_hi = min(ke - 1, hi_of(iq_hi));
-  const int full_lo = max(kb, lo_of(iq_hi));
-  const int full_hi = min(ke - 1, hi_of(iq_lo));
-  const int my_lo = max(kb, lo_of(iq));
-  const int my_hi = min(ke - 1, hi_of(iq));
+  // the tile's key ranges are uniform; readfirstlane keeps them (and the
+  // buffer descriptors built from them) in scalar registers
+  const int tile_lo = __builtin_amdgcn_readfirstlane(max(kb, lo_of(iq_lo)));
+  const int tile_hi = __builtin_amdgcn_readfirstlane(min(ke - 1, hi_of(iq_hi)));
+  const int full_lo = __builtin_amdgcn_readfirstlane(max(kb, lo_of(iq_hi)));
+  const int full_hi = __builtin_amdgcn_readfirstlane(min(ke - 1, hi_of(iq_lo)));
+  int my_lo[RT], my_hi[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    my_lo[rt] = max(kb, lo_of(iq[rt]));
+    my_hi[rt] = min(ke - 1, hi_of(iq[rt]));
+  }
   const int j_begin = (tile_lo / C::BN) * C::BN;
   const int j_end = tile_hi + 1;
   const int n_iter = j_end > j_begin ? (j_end - j_begin + C::BN - 1) / C::BN : 0;
 
-  f32x16 acc[C::TV];
+  f32x16 acc[RT][C::TV];
 #pragma unroll
-  for (int t = 0; t < C::TV; ++t)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+    for (int t = 0; t < C::TV; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rt][t][e] = 0.f;
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+  }
 
   // One K (or V) block = NWM * KL buffer->LDS loads of 1 KiB (RPL rows each);
   // wave wm issues loads [wm*KL, (wm+1)*KL).  Lane l of a load writes LDS
@@ -341,6 +371,7 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   block_barrier();
 
   // descriptor of key block jb: rows [jb, min(jb + BN, j_end)) of K or V
+  // (all uniform: built in scalar registers)
   auto block_rsrc = [&](const char* base, int64_t st, int jb) {
     const int rows_left = min(j_end - jb, C::BN);
     const int nb = rows_left > 0 ? (rows_left - 1) * (int)st + C::ROWB : 0;
@@ -369,15 +400,16 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   // P of a key block, packed for the PV MFMA (group g: keys 16g..16g+15):
   // pbuf[it % 2] holds P(it), so P(it) is produced while PV(it-1) still reads
   // P(it-1)
-  u32x4 pbuf[2][C::NG];
+  u32x4 pbuf[2][RT][C::NG];
 
   // O^T += V^T P^T for one key block from V stage VST with P from pb.  Lane
   // 4e+jq of 16-lane group (hl, grp) reads row 16g+8q+4hl+e, columns
   // 32t+16grp+4jq..+3, and receives column lr of those 4 rows.  All fragments
-  // of the block are read up front (two reads per MFMA n = (group g, tile t)),
-  // and MFMA n waits only for its own two; `between(n)` is VALU work placed
-  // after MFMA n.
-  auto pv = [&](auto VST_, const u32x4 (&pb)[C::NG], auto&& between) {
+  // of the block are read up front (two reads per fragment n = (group g,
+  // tile t)); fragment n feeds one MFMA per row tile, which wait only for
+  // its own two reads; `between(n)` is VALU work placed after fragment n's
+  // MFMAs.
+  auto pv = [&](auto VST_, const u32x4 (&pb)[RT][C::NG], auto&& between) {
     constexpr int VST = decltype(VST_)::value;
     constexpr int NM = C::NG * C::TV;
     static_assert(2 * NM - 2 <= 15, "lgkmcnt range");
@@ -393,15 +425,17 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
       tie(vr[n][0]);
       tie(vr[n][1]);
       const u32x4 vf = {(uint32_t)vr[n][0].x, (uint32_t)vr[n][0].y, (uint32_t)vr[n][1].x, (uint32_t)vr[n][1].y};
-      acc[t] = mfma32<DT>(acc[t], vf, pb[g]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma32<DT>(acc[rt][t], vf, pb[rt][g]);
       between(int_c<n>{});
     });
   };
 
   // S^T = K Q^T for one key block from K stage KST into sd, tile-major, one
-  // MFMA per chunk; MFMA n takes its K fragment from slot n % KR of a ring
-  // filled KR - 1 MFMAs ahead; `between(n)` is VALU work placed after MFMA n.
-  auto qk = [&](auto KST_, f32x16 (&sd)[C::NT], auto&& between) {
+  // K fragment per chunk feeding one MFMA per row tile; fragment n comes from
+  // slot n % KR of a ring filled KR - 1 fragments ahead; `between(n)` is VALU
+  // work placed after fragment n's MFMAs.
+  auto qk = [&](auto KST_, f32x16 (&sd)[RT][C::NT], auto&& between) {
     constexpr int KST = decltype(KST_)::value;
     constexpr int NM = C::NT * C::KS;
     constexpr int KR = 5;
@@ -419,18 +453,79 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
       // reads issued after fragment n: min(KR - 1, NM - 1 - n)
       lgkm_wait<(NM - 1 - n < KR - 1 ? NM - 1 - n : KR - 1)>();
       tie(kf[n % KR]);
-      if constexpr (k == 0) {
-        f32x16 z;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) z[e] = 0.f;
-        sd[u] = mfma32<DT>(z, kf[n % KR], qf[k]);
-      } else {
-        sd[u] = mfma32<DT>(sd[u], kf[n % KR], qf[k]);
+      for (int rt = 0; rt < RT; ++rt) {
+        if constexpr (k == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) z[e] = 0.f;
+          sd[rt][u] = mfma32<DT>(z, kf[n % KR], qf[rt][k]);
+        } else {
+          sd[rt][u] = mfma32<DT>(sd[rt][u], kf[n % KR], qf[rt][k]);
+        }
       }
       between(int_c<n>{});
     });
   };
   auto nothing = [](auto) {};
+
+  // PV(it-1) and QK(it+1) of one iteration interleaved on the MFMA pipe, in
+  // the order PV0 QK0 PV1 QK1 ...: the QK accumulation chain (one S^T tile,
+  // KS dependent MFMAs) and the PV chains fill each other's latency, and the
+  // LDS reads are issued in the order the MFMAs consume them (PV fragment n =
+  // two transpose reads, QK fragment n = one read), kPvqkAhead reads ahead of
+  // need, each MFMA waiting only for its own reads.  `between(j)` is VALU
+  // work placed after MFMA j.
+  auto pvqk = [&](auto VST_, const u32x4 (&pb)[RT][C::NG], auto KST_, f32x16 (&sd)[RT][C::NT], auto&& between) {
+    constexpr int VST = decltype(VST_)::value, KST = decltype(KST_)::value;
+    constexpr int NM = C::NG * C::TV;
+    static_assert(NM == C::NT * C::KS, "as many PV as QK fragments");
+    constexpr int NR = 3 * NM;
+    i32x2 vr[NM][2];
+    u32x4 kf[NM];
+    auto issue = [&](auto R_) {
+      constexpr int r = decltype(R_)::value, n = r / 3, kind = r % 3;
+      if constexpr (kind < 2) {
+        constexpr int g = n / C::TV, t = n % C::TV;
+        vr[n][kind] = lds_tr16<VST * C::TILE + (16 * g + 8 * kind) * C::ROWB>(vx[t]);
+      } else {
+        constexpr int u = n / C::KS, k = n % C::KS;
+        kf[n] = lds_b128<KST * C::TILE>(kx[u][k]);
+      }
+    };
+    static_for<pvqk_issued(0, NR)>([&](auto R_) { issue(R_); });
+    static_for<2 * NM>([&](auto J_) {
+      constexpr int j = decltype(J_)::value, n = j / 2;
+      if constexpr (j > 0) {
+        constexpr int from = pvqk_issued(j - 1, NR);
+        static_for<pvqk_issued(j, NR) - from>([&](auto D_) { issue(int_c<from + decltype(D_)::value>{}); });
+      }
+      lgkm_wait<pvqk_issued(j, NR) - pvqk_need(j)>();
+      if constexpr (j % 2 == 0) {
+        constexpr int g = n / C::TV, t = n % C::TV;
+        tie(vr[n][0]);
+        tie(vr[n][1]);
+        const u32x4 vf = {(uint32_t)vr[n][0].x, (uint32_t)vr[n][0].y, (uint32_t)vr[n][1].x, (uint32_t)vr[n][1].y};
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][t] = mfma32<DT>(acc[rt][t], vf, pb[rt][g]);
+      } else {
+        constexpr int u = n / C::KS, k = n % C::KS;
+        tie(kf[n]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          if constexpr (k == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) z[e] = 0.f;
+            sd[rt][u] = mfma32<DT>(z, kf[n], qf[rt][k]);
+          } else {
+            sd[rt][u] = mfma32<DT>(sd[rt][u], kf[n], qf[rt][k]);
+          }
+        }
+      }
+      between(int_c<j>{});
+    });
+  };
 
   // Ring of NS = 4 stages for K and for V: K(b) in K stage b%4, V(b) in V
   // stage b%4.  Iteration it issues K(it+4) and V(it+2) and needs K(it+1)
@@ -439,7 +534,7 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   // the same order as iterations -4..-1 would (with empty loads for V(-2) and
   // V(-1)), so the count is uniform.
   static_assert(C::NS == 4, "ring schedule");
-  f32x16 sbuf[2][C::NT];  // S of block it in sbuf[it % 2]
+  f32x16 sbuf[2][RT][C::NT];  // S of block it in sbuf[it % 2]
   const int jlast = j_begin + n_iter * C::BN;  // first block past the tile's range
   if (n_iter > 0) {
     issue_k(j_begin, int_c<0>{});
@@ -463,8 +558,8 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   // rescaled, and the block's exponentials recomputed.  The row sum adds the
   // fp32 p (the LSE needs them unrounded).
   constexpr float kSumLimit = 4096.0f;  // 2^12: P stays far inside fp16 range
-  constexpr int NPV = C::NG * C::TV, NQK = C::NT * C::KS;  // MFMAs per phase
-  constexpr int NWD = 8 * C::NT;                           // packed P words per block
+  constexpr int NPV = C::NG * C::TV, NQK = C::NT * C::KS;  // fragments per phase
+  constexpr int NWD = 8 * C::NT;                           // packed P words per block and row tile
   auto exp_word = [&](const f32x16 (&sd)[C::NT], u32x4 (&pb)[C::NG], float nb, float& rs, auto W_) {
     constexpr int w = decltype(W_)::value, i = 2 * w;  // elements i, i + 1
     float p0 = fast_exp2(__builtin_fmaf(sd[i >> 4][i & 15], scale_log2, nb));
@@ -475,8 +570,9 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
     rs += p0 + p1;
     tie(rs);
   };
-  // words of P done after VALU slot k of NPV + NQK slots (spread evenly)
-  auto words_upto = [](int k) { return (k * NWD) / (NPV + NQK); };
+  // words of P (all row tiles, RT * NWD) done after VALU slot k of NPV + NQK
+  // slots (spread evenly)
+  auto words_upto = [](int k) { return (k * RT * NWD) / (NPV + NQK); };
 
   // ST = it % 4 at compile time: every LDS stage offset is an immediate.
   // FIRST: it == 0 (no PV of a previous block; the reference is set from the
@@ -493,58 +589,72 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
     block_barrier();
     issue_k(j0 + 4 * C::BN, int_c<ST>{});
     issue_v(j0 + 2 * C::BN, int_c<(ST + 2) % 4>{});
-    f32x16 (&s)[C::NT] = sbuf[SB];
-    u32x4 (&pc)[C::NG] = pbuf[SB];
+    f32x16 (&s)[RT][C::NT] = sbuf[SB];
+    u32x4 (&pc)[RT][C::NG] = pbuf[SB];
 
     const bool full = j0 >= full_lo && j0 + C::BN - 1 <= full_hi;
     if (!full) {
 #pragma unroll
-      for (int u = 0; u < C::NT; ++u)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = j0 + 32 * u + 8 * (e >> 2) + 4 * hl + (e & 3);
-          if (j < my_lo || j > my_hi) s[u][e] = -INFINITY;
-        }
+        for (int u = 0; u < C::NT; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = j0 + 32 * u + 8 * (e >> 2) + 4 * hl + (e & 3);
+            if (j < my_lo[rt] || j > my_hi[rt]) s[rt][u][e] = -INFINITY;
+          }
     }
-    auto row_max = [&]() {
+    auto row_max = [&](int rt) {
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < C::NT; ++u)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[rt][u][e]);
       return max_halves(mx) * scale_log2;  // scale > 0 commutes with max
     };
-    if constexpr (FIRST) m_run = row_max();
-    const float nbase = -(m_run == -INFINITY ? 0.f : m_run);
-    float rs = 0.f;
+    if constexpr (FIRST) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) m_run[rt] = row_max(rt);
+    }
+    float nbase[RT], rs[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      nbase[rt] = -(m_run[rt] == -INFINITY ? 0.f : m_run[rt]);
+      rs[rt] = 0.f;
+    }
     // the exponentials of block it are spread over the VALU slots after the
-    // MFMAs of PV(it-1) and QK(it+1)
+    // MFMAs of PV(it-1) and QK(it+1); word w of the RT * NWD words belongs to
+    // row tile w / NWD
     auto slot = [&](auto K_) {
       constexpr int k = decltype(K_)::value;
       static_for<words_upto(k + 1) - words_upto(k)>([&](auto W_) {
-        exp_word(s, pc, nbase, rs, int_c<words_upto(k) + decltype(W_)::value>{});
+        constexpr int w = words_upto(k) + decltype(W_)::value, rt = w / NWD;
+        exp_word(s[rt], pc[rt], nbase[rt], rs[rt], int_c<w % NWD>{});
       });
     };
     if constexpr (!FIRST) {
-      pv(int_c<(ST + 3) % 4>{}, pbuf[SB ^ 1], [&](auto N_) { slot(N_); });
+      pvqk(int_c<(ST + 3) % 4>{}, pbuf[SB ^ 1], int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(N_); });
     } else {
       static_for<NPV>([&](auto N_) { slot(N_); });
+      qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(int_c<NPV + decltype(N_)::value>{}); });
     }
-    qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(int_c<NPV + decltype(N_)::value>{}); });
     // reference check (see above); has_keys: the row sees a key of this block
-    const bool has_keys = my_lo <= j0 + C::BN - 1 && my_hi >= j0 && my_lo <= my_hi;
-    if (__any(rs > kSumLimit || (m_run == -INFINITY && has_keys))) {
-      const float m_new = fmaxf(m_run, row_max());
-      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < C::TV; ++t) acc[t] *= alpha;
-      m_run = m_new;
-      const float nb2 = -(m_run == -INFINITY ? 0.f : m_run);
-      rs = 0.f;
-      static_for<NWD>([&](auto W_) { exp_word(s, pc, nb2, rs, W_); });
+    for (int rt = 0; rt < RT; ++rt) {
+      const bool has_keys = my_lo[rt] <= j0 + C::BN - 1 && my_hi[rt] >= j0 && my_lo[rt] <= my_hi[rt];
+      if (__any(rs[rt] > kSumLimit || (m_run[rt] == -INFINITY && has_keys))) {
+        const float m_new = fmaxf(m_run[rt], row_max(rt));
+        const float alpha = fast_exp2(m_run[rt] - (m_new == -INFINITY ? 0.f : m_new));
+        l_run[rt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < C::TV; ++t) acc[rt][t] *= alpha;
+        m_run[rt] = m_new;
+        const float nb2 = -(m_run[rt] == -INFINITY ? 0.f : m_run[rt]);
+        rs[rt] = 0.f;
+        static_for<NWD>([&](auto W_) { exp_word(s[rt], pc[rt], nb2, rs[rt], W_); });
+      }
+      l_run[rt] += rs[rt];
     }
-    l_run += rs;
   };
 
   if (n_iter > 0) {
@@ -573,37 +683,42 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
     }
   }
 
-  // ---- epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
-  const bool live = l_tot > 0.f;
-  const float inv = live ? 1.0f / l_tot : 0.f;
-  const float lse_v = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  if (S > 1) {
-    const int64_t tglob = (int64_t)q_off + iq;
-    float* op = p.o_part + (((int64_t)split * p.total_q + tglob) * p.hq + hq) * C::D;
+  // ---- epilogue, per row tile
 #pragma unroll
-    for (int t = 0; t < C::TV; ++t)
+  for (int rt = 0; rt < RT; ++rt) {
+    const float l_tot = l_run[rt] + __shfl_xor(l_run[rt], 32);
+    if (!row_ok[rt]) continue;
+    const bool live = l_tot > 0.f;
+    const float inv = live ? 1.0f / l_tot : 0.f;
+    const float lse_v = live ? (m_run[rt] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (S > 1) {
+      const int64_t tglob = (int64_t)q_off + iq[rt];
+      float* op = p.o_part + (((int64_t)split * p.total_q + tglob) * p.hq + hq[rt]) * C::D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 o = {acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv, acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv};
-        *(f32x4*)(op + 32 * t + 8 * j + 4 * hl) = o;
+      for (int t = 0; t < C::TV; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 o = {acc[rt][t][4 * j] * inv, acc[rt][t][4 * j + 1] * inv, acc[rt][t][4 * j + 2] * inv,
+                     acc[rt][t][4 * j + 3] * inv};
+          *(f32x4*)(op + 32 * t + 8 * j + 4 * hl) = o;
+        }
+      if (hl == 0) p.lse_part[((int64_t)split * p.hq + hq[rt]) * p.total_q + tglob] = lse_v;
+    } else {
+      char* op = p.o + (p.cu_q ? (int64_t)(q_off + iq[rt]) * p.o_st : (int64_t)b * p.o_sb + (int64_t)iq[rt] * p.o_st) +
+                 (int64_t)hq[rt] * p.o_sh;
+#pragma unroll
+      for (int t = 0; t < C::TV; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x2 w = {pack2_in<DT>(acc[rt][t][4 * j] * inv, acc[rt][t][4 * j + 1] * inv),
+                     pack2_in<DT>(acc[rt][t][4 * j + 2] * inv, acc[rt][t][4 * j + 3] * inv)};
+          *(u32x2*)(op + (32 * t + 8 * j + 4 * hl) * 2) = w;
+        }
+      if (p.lse && hl == 0) {
+        const int64_t li = p.cu_q ? (int64_t)hq[rt] * p.lse_sh + q_off + iq[rt]
+                                  : (int64_t)b * p.lse_sb + (int64_t)hq[rt] * p.lse_sh + iq[rt];
+        p.lse[li] = lse_v;
       }
-    if (hl == 0) p.lse_part[((int64_t)split * p.hq + hq) * p.total_q + tglob] = lse_v;
-  } else {
-    char* op = p.o + (p.cu_q ? (int64_t)(q_off + iq) * p.o_st : (int64_t)b * p.o_sb + (int64_t)iq * p.o_st) +
-               (int64_t)hq * p.o_sh;
-#pragma unroll
-    for (int t = 0; t < C::TV; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w = {pack2_in<DT>(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
-                   pack2_in<DT>(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
-        *(u32x2*)(op + (32 * t + 8 * j + 4 * hl) * 2) = w;
-      }
-    if (p.lse && hl == 0) {
-      const int64_t li = p.cu_q ? (int64_t)hq * p.lse_sh + q_off + iq : (int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + iq;
-      p.lse[li] = lse_v;
     }
   }
 }
