@@ -47,7 +47,10 @@ struct DecCfg {
   static constexpr int CQK = DQK * BYTES / 64;     // 16-byte chunks per lane per key tile
   static constexpr int TV = DV / 16;               // O^T tiles
   static constexpr int VROW = DV * BYTES;          // bytes per V row
-  static constexpr int VP = VROW + 16;             // LDS pitch of a V row
+  // LDS pitch of a V row: +32 bytes makes both the 16-byte row writes and the
+  // 8-byte transpose reads of 2-byte types free of bank conflicts (+16 left
+  // the reads two-way conflicted); 1-byte rows have no conflict-free pitch
+  static constexpr int VP = VROW + (BYTES == 2 ? 32 : 16);
   static constexpr int VCH = BN * VROW / (64 * 16);  // 16-byte V loads per lane per block
   static constexpr int VROWS_PER_LOAD = 64 * 16 / VROW;
   static constexpr int LDS_V = NW * BN * VP;
