@@ -360,15 +360,9 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
 #pragma unroll
   for (int t = 0; t < C::TV; ++t) vx[t] = lds0 + (uint32_t)(C::NS * C::TILE + (vaddr ^ (64 * t)));
 
-  // zero the LDS once so no slot is ever read uninitialised
-#pragma unroll
-  for (int i = tid * 16; i < C::LDS; i += C::NTHR * 16) *(u32x4*)(smem + i) = u32x4{0u, 0u, 0u, 0u};
-  // The zero stores must land before any buffer->LDS load of another wave
-  // does: wait for them (lgkmcnt), then a bare barrier.  __syncthreads()
-  // would also wait for the Q loads in flight (vmcnt(0)), putting their
-  // latency in front of the first K/V loads.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  block_barrier();
+  // No LDS initialisation: every K and V slot of a stage is written by the
+  // block's loads (rows past the tile's range and blocks past it as zeros)
+  // before any wave reads it, so the prologue's loads go out at once.
 
   // descriptor of key block jb: rows [jb, min(jb + BN, j_end)) of K or V
   // (all uniform: built in scalar registers)
