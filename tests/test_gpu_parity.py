@@ -258,6 +258,43 @@ def test_combine_kernel_on_oracle_partials(fmha, oracle):
     assert np.abs(go[~np.isnan(ref_o)] - ref_o[~np.isnan(ref_o)]).max() < 1e-5
 
 
+@pytest.mark.parametrize("num_splits,dv,lens_q", [
+    (6, 64, [2, 1]),        # few rows: narrowest column groups, one partial row per thread
+    (100, 128, [3, 2]),     # few rows, many splits: several partial rows per thread
+    (256, 128, [40, 30]),   # many rows: widest groups capped so a thread owns <= 16 rows
+    (256, 256, [2, 1]),     # widest Dv, most splits
+    (37, 256, [40, 30]),
+])
+def test_combine_shapes(fmha, oracle, num_splits, dv, lens_q):
+    # the combine's grid shapes (column-group width, partial rows per thread)
+    # on oracle partials: every split of every row, fp32
+    chunk = 4
+    lens_k = [num_splits * chunk - 3, (num_splits * chunk) // 3]
+    prob = make_problem(f"combine_{num_splits}_{dv}", dtype="f32", lens_q=lens_q, lens_k=lens_k,
+                        hq=4, hkv=4, dqk=dv, dv=dv, seed=12, varlen_q=True, varlen_k=True)
+    scale = 1 / math.sqrt(dv)
+    parts = [oracle.split_attention(raw_bits(prob.q), raw_bits(prob.k), raw_bits(prob.v),
+                                    "f32", chunk=chunk, split=s, cu_q=prob.cu_q,
+                                    cu_k=prob.cu_k, scale=scale)
+             for s in range(num_splits)]
+    o_part = np.stack([p[0] for p in parts]).astype(np.float32)
+    l_part = np.stack([p[1] for p in parts]).astype(np.float32)
+    ref_o, ref_l = oracle.combine(o_part.astype(np.float64), l_part.astype(np.float64),
+                                  chunk=chunk, cu_q=prob.cu_q, cu_k=prob.cu_k)
+    dev = upload(prob)
+    out, lse = alloc_outputs(prob, dev)
+    op = torch.from_numpy(np.nan_to_num(o_part, nan=0.0)).cuda()
+    lp = torch.from_numpy(np.nan_to_num(l_part, nan=-np.inf)).cuda()
+    announce(f"combine shapes S={num_splits} dv={dv} lens_q={lens_q}")
+    fmha.splitkv_combine(op, lp, split_chunk=chunk, out=out, lse=lse,
+                         cu_seqlens_q=dev["cu_seqlens_q"], cu_seqlens_k=dev["cu_seqlens_k"],
+                         max_seqlen_q=dev["max_seqlen_q"])
+    torch.cuda.synchronize()
+    go, gl = to_packed(prob, out, lse)
+    compare(prob, go, gl, ref_o, ref_l, what=f"combine S={num_splits} dv={dv}")
+    assert np.abs(go - ref_o).max() < 1e-5
+
+
 # ---- determinism, graph replay, guard bands, errors -------------------------
 
 def test_determinism(fmha):
