@@ -264,12 +264,17 @@ def test_combine_kernel_on_oracle_partials(fmha, oracle):
     (256, 128, [40, 30]),   # many rows: widest groups capped so a thread owns <= 16 rows
     (256, 256, [2, 1]),     # widest Dv, most splits
     (37, 256, [40, 30]),
+    # many rows, few partials: one wave per row
+    (20, 128, [40, 30]),
+    (6, 64, [40, 30]),
+    (16, 256, [40, 30]),
+    (3, 128, [70]),
 ])
 def test_combine_shapes(fmha, oracle, num_splits, dv, lens_q):
     # the combine's grid shapes (column-group width, partial rows per thread)
     # on oracle partials: every split of every row, fp32
     chunk = 4
-    lens_k = [num_splits * chunk - 3, (num_splits * chunk) // 3]
+    lens_k = [num_splits * chunk - 3, (num_splits * chunk) // 3][:len(lens_q)]
     prob = make_problem(f"combine_{num_splits}_{dv}", dtype="f32", lens_q=lens_q, lens_k=lens_k,
                         hq=4, hkv=4, dqk=dv, dv=dv, seed=12, varlen_q=True, varlen_k=True)
     scale = 1 / math.sqrt(dv)
