@@ -193,6 +193,9 @@ typedef struct fmha_fwd_plan {
   size_t workspace_bytes;
   size_t o_part_offset;
   size_t lse_part_offset;
+  int32_t tile_order;   /* 0: tiles grouped by (sequence, kv head); 1: all tiles
+                           longest first (32-row-tile prefill kernels, one split,
+                           causal or a right-only window, batch <= 64) */
 } fmha_fwd_plan;
 
 /*

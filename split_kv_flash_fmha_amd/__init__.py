@@ -70,6 +70,7 @@ class Plan(ctypes.Structure):
         ("num_q_tiles", _i32), ("key_block", _i32), ("kernel_id", _i32),
         ("grid_main", _i64), ("grid_combine", _i64),
         ("workspace_bytes", _sz), ("o_part_offset", _sz), ("lse_part_offset", _sz),
+        ("tile_order", _i32),
     ]
 
     def as_dict(self):

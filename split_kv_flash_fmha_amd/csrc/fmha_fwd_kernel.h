@@ -138,19 +138,38 @@ __device__ __forceinline__ u32x4 pack_p(const f32x4* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Work item (split, kv head, sequence, query tile) of this workgroup.
-// Items are ordered so that the query tiles and splits of one (sequence, kv
-// head) -- the workgroups that stream the same K and V -- form one group of
-// consecutive items, query tiles in descending order (in a causal tile the
-// later rows see more keys, so the longest items start first).  Workgroups go
-// to the 8 XCDs round-robin (block i on XCD i % 8) and each XCD has its own L2:
-// groups are dealt to XCDs in rounds of 8, a whole group to one XCD, so the
-// workgroups sharing K and V run on one XCD at about the same time.  A last
-// round of fewer than 8 groups is dealt block by block.
+// Work item of this workgroup: (split, kv head, sequence, query tile) and the
+// sequence's query / key offsets and lengths.
 struct WorkItem {
   int split, hkv, b, qtile;
+  int q_off, sq, k_off, sk;
 };
-__device__ __forceinline__ WorkItem work_item(const FwdParams& p) {
+
+__device__ __forceinline__ void seq_span(const FwdParams& p, int b, WorkItem& w) {
+  int q0 = b * p.seqlen_q, q1 = q0 + p.seqlen_q, k0 = b * p.seqlen_k, k1 = k0 + p.seqlen_k;
+  if (p.cu_q || p.cu_k) {
+    // the four loads are issued together (one round trip)
+    const int32_t* cq = p.cu_q ? p.cu_q : p.cu_k;
+    const int32_t* ck = p.cu_k ? p.cu_k : p.cu_q;
+    const int a0 = cq[b], a1 = cq[b + 1], c0 = ck[b], c1 = ck[b + 1];
+    if (p.cu_q) q0 = a0, q1 = a1;
+    if (p.cu_k) k0 = c0, k1 = c1;
+  }
+  w.q_off = q0;
+  w.sq = q1 - q0;
+  w.k_off = k0;
+  w.sk = k1 - k0;
+}
+
+// Grouped order (kTileOrderGrouped).  Items are ordered so that the query
+// tiles and splits of one (sequence, kv head) -- the workgroups that stream the
+// same K and V -- form one group of consecutive items, query tiles in
+// descending order.  Workgroups go to the 8 XCDs round-robin (block i on XCD
+// i % 8) and each XCD has its own L2: groups are dealt to XCDs in rounds of 8,
+// a whole group to one XCD, so the workgroups sharing K and V run on one XCD
+// at about the same time.  A last round of fewer than 8 groups is dealt block
+// by block.
+__device__ __forceinline__ WorkItem grouped_item(const FwdParams& p) {
   constexpr uint32_t kXcds = 8;
   const uint32_t bid = blockIdx.x;
   const uint32_t gsz = (uint32_t)p.num_q_tiles * (uint32_t)p.num_splits;  // items per group
@@ -169,7 +188,107 @@ __device__ __forceinline__ WorkItem work_item(const FwdParams& p) {
   item /= (uint32_t)p.num_splits;
   w.hkv = (int)(item % (uint32_t)p.hkv);
   w.b = (int)(item / (uint32_t)p.hkv);
+  seq_span(p, w.b, w);
   return w;
+}
+
+// Inclusive prefix sum of v over the lanes of the wave: a scan within each
+// row of 16 lanes (DPP row shifts by 1, 2, 4, 8), then the last lane of row 0
+// (1) is added to rows 1 and 3 (2 and 3) by the row broadcasts.
+__device__ __forceinline__ int wave_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_scan(v), 63); }
+
+// Longest-first order (kTileOrderLongestFirst): one split, no left window, at
+// most 64 sequences (lane b of every wave holds sequence b).
+//
+// The hardware hands block i to XCD i % 8 and, within it, to shader engine
+// (i / 8) % 4, each with a fixed number of workgroup slots; every such lane
+// starts its blocks in order as slots free up.  Sorting all tiles by cost,
+// longest first, gives the 32 lanes near-identical cost sequences (consecutive
+// blocks cost about the same) and makes each lane's in-order start a
+// longest-processing-time-first schedule.  Under a causal mask the tiles of one
+// sequence differ in cost; with skewed lengths whole sequences do, and a fixed
+// (sequence, tile) -> lane pattern leaves some lanes with far more work.
+//
+// The cost class of a tile is 1 + ceil(keys / 64), keys = the keys its last
+// row attends (0 for a row before the first key: the tile still writes its
+// rows); the tiles of one sequence with class >= c form a suffix of its query
+// tiles, so the number of items in class >= c has a closed form per sequence.
+// Position blockIdx.x is found by a binary search over the class, then by a
+// prefix sum over sequences.  Within a class the order is sequence, query tile
+// (descending), kv head: with a multiple of 8 kv heads every tile of a
+// (sequence, kv head) lands on the same XCD.  Positions past the last tile
+// return false.
+template <int ROWS>
+__device__ __forceinline__ bool longest_first_item(const FwdParams& p, WorkItem& w) {
+  constexpr int kUnit = 64;  // keys per cost unit
+  const int lane = threadIdx.x & 63;
+  const bool real = lane < p.batch;
+  WorkItem sp;
+  seq_span(p, real ? lane : p.batch - 1, sp);  // clamped: every lane loads in bounds
+  const int q0 = sp.q_off, k0 = sp.k_off;
+  const int sq = real ? sp.sq : 0, sk = real ? sp.sk : 0;
+  const int G = p.group;
+  const int nt = (sq > 0 && sk > 0) ? (sq * G + ROWS - 1) / ROWS : 0;  // query tiles
+  const int diag = sk - sq + p.wr;  // a row i attends keys <= i + diag (wr >= 0)
+  const bool bounded = p.wr >= 0;
+  // number of this sequence's tiles with cost class >= c (branch-free; class
+  // 1 (need <= 0) holds every tile; a product that wraps is discarded by the
+  // last select)
+  auto count = [&](int c) -> int {
+    const int need = (c - 2) * kUnit + 1;             // keys the last row must attend
+    const int t = max(need - 1 - diag, 0);            // first query row attending them
+    const unsigned f = (unsigned)t * (unsigned)G / (unsigned)ROWS;
+    const int first = (bounded && need > 0) ? (int)min(f, (unsigned)nt) : 0;
+    return need > sk ? 0 : nt - first;
+  };
+  const int H = p.hkv;
+  const int pos = blockIdx.x;
+  if (pos >= H * wave_sum(nt)) return false;
+  int lo = 1, hi = 2 + (p.max_seqlen_k + kUnit - 1) / kUnit;  // items(lo) > pos >= items(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (H * wave_sum(count(mid)) > pos)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int above = count(lo + 1);
+  const int j = pos - H * wave_sum(above);  // index within class lo
+  const int kc = count(lo) - above;         // this sequence's tiles in class lo
+  const int excl = wave_scan(kc) - kc;      // tiles of class lo in lower sequences
+  const uint64_t sel = __ballot(kc > 0 && H * excl <= j && j < H * (excl + kc));
+  if (sel == 0) return false;  // not reached: the ranges partition the class
+  // (whatever excl holds, the selected lane's test bounds jj to [0, H * kc),
+  // so the tile and head below are in range)
+  const int b = (int)__builtin_ctzll(sel);
+  const int jj = j - H * __builtin_amdgcn_readlane(excl, b);
+  w.split = 0;
+  w.b = b;
+  w.hkv = jj % H;
+  w.qtile = __builtin_amdgcn_readlane(nt - above, b) - 1 - jj / H;
+  w.q_off = __builtin_amdgcn_readlane(q0, b);
+  w.sq = __builtin_amdgcn_readlane(sq, b);
+  w.k_off = __builtin_amdgcn_readlane(k0, b);
+  w.sk = __builtin_amdgcn_readlane(sk, b);
+  return true;
+}
+
+// This workgroup's item; false: nothing to do.
+template <int ROWS>
+__device__ __forceinline__ bool work_item(const FwdParams& p, WorkItem& w) {
+  if (p.tile_order == kTileOrderLongestFirst) return longest_first_item<ROWS>(p, w);
+  w = grouped_item(p);
+  return true;
 }
 
 // Per-tensor fp8 scale: *ptr, or 1 when ptr is null.  The load is made
@@ -254,25 +373,11 @@ __global__ __launch_bounds__(C::NTHR) void fmha_fwd_kernel(FwdParams p) {
 
   // ---- tile decode: split fastest, then kv head, batch, query tile (reversed,
   // so the heaviest tiles of causal / long sequences are dispatched first)
-  const WorkItem wi = work_item(p);
+  WorkItem wi;
+  if (!work_item<16 * C::NWM>(p, wi)) return;
   const int S = p.num_splits;
   const int split = wi.split, hkv = wi.hkv, b = wi.b, qtile = wi.qtile;
-
-  int q_off, sq, k_off, sk;
-  if (p.cu_q) {
-    q_off = p.cu_q[b];
-    sq = p.cu_q[b + 1] - q_off;
-  } else {
-    q_off = b * p.seqlen_q;
-    sq = p.seqlen_q;
-  }
-  if (p.cu_k) {
-    k_off = p.cu_k[b];
-    sk = p.cu_k[b + 1] - k_off;
-  } else {
-    k_off = b * p.seqlen_k;
-    sk = p.seqlen_k;
-  }
+  const int q_off = wi.q_off, sq = wi.sq, k_off = wi.k_off, sk = wi.sk;
   const int G = p.group;
   const int rows = sq * G;
   const int row0 = qtile * 16 * C::NWM;

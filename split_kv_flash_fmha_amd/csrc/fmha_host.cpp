@@ -283,6 +283,19 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     pl.workspace_bytes = 0;
   }
   pl.grid_main = r->empty ? 0 : (int64_t)S * units;
+  // longest-first tile order where the tiles of a sequence differ in cost (a
+  // right-bounded mask: causal) and the kernel's per-workgroup search applies
+  // (one split, no left window, at most 64 sequences).  Its grid covers every
+  // tile that exists, a bound from the packed query count (sequence b has
+  // ceil(rows_b / tile) tiles).
+  pl.tile_order = kTileOrderGrouped;
+  if (prefill && S == 1 && pl.window_right >= 0 && pl.window_left < 0 &&
+      a->batch <= kLongestFirstMaxBatch && !r->empty) {
+    pl.tile_order = kTileOrderLongestFirst;
+    const int64_t tiles = (r->total_q * G + (int64_t)a->batch * (pl.rows_per_tile - 1)) / pl.rows_per_tile;
+    const int64_t slots = (int64_t)a->batch * pl.num_q_tiles;
+    pl.grid_main = (int64_t)a->num_heads_kv * (tiles < slots ? tiles : slots);
+  }
   if (pl.grid_main >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
   pl.grid_combine = (r->empty || S == 1) ? 0 : combine_grid(a->head_dim_v, S, r->sq_max * a->num_heads_q * a->batch);
   if (pl.grid_combine >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
@@ -341,6 +354,8 @@ FwdParams make_params(const fmha_fwd_args* a, const Resolved& r) {
   p.chunk = r.plan.split_chunk;
   p.num_q_tiles = r.plan.num_q_tiles;
   p.out_dtype = a->out_dtype;
+  p.tile_order = r.plan.tile_order;
+  p.max_seqlen_k = (int32_t)r.sk_max;
   return p;
 }
 

@@ -40,7 +40,14 @@ struct FwdParams {
   int32_t chunk;       // keys per split
   int32_t num_q_tiles;
   int32_t out_dtype;
+  int32_t tile_order;    // kTileOrder*
+  int32_t max_seqlen_k;  // bound on any sequence's key count
 };
+
+// Block -> tile orders of the attention launch.
+constexpr int32_t kTileOrderGrouped = 0;       // by (sequence, kv head), XCD-grouped
+constexpr int32_t kTileOrderLongestFirst = 1;  // all tiles by cost, longest first
+constexpr int kLongestFirstMaxBatch = 64;      // one sequence per lane of a wave
 
 struct CombineParams {
   const float* o_part;

@@ -84,25 +84,11 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   const int hl = lane >> 5;
   const int lr = lane & 31;
 
-  const WorkItem wi = work_item(p);
+  WorkItem wi;
+  if (!work_item<C::ROWS>(p, wi)) return;
   const int S = p.num_splits;
   const int split = wi.split, hkv = wi.hkv, b = wi.b, qtile = wi.qtile;
-
-  int q_off, sq, k_off, sk;
-  if (p.cu_q) {
-    q_off = p.cu_q[b];
-    sq = p.cu_q[b + 1] - q_off;
-  } else {
-    q_off = b * p.seqlen_q;
-    sq = p.seqlen_q;
-  }
-  if (p.cu_k) {
-    k_off = p.cu_k[b];
-    sk = p.cu_k[b + 1] - k_off;
-  } else {
-    k_off = b * p.seqlen_k;
-    sk = p.seqlen_k;
-  }
+  const int q_off = wi.q_off, sq = wi.sq, k_off = wi.k_off, sk = wi.sk;
   const int G = p.group;
   const int rows = sq * G;
   const int row0 = qtile * C::ROWS;

@@ -137,6 +137,35 @@ def test_varlen_prefill_full_sampled(fmha, oracle, lengths, causal):
     # properties at every row: finite, |O| bounded by max |V| of the sequence
     assert np.isfinite(go).all() and np.isfinite(gl).all()
     assert np.abs(go).max() <= float(prob.v.abs().max()) + 1e-3
+    # every row has a key here: every LSE is written (no tile left out)
+    assert (gl != SENTINEL_LSE).all()
+
+
+# ---- tile orders: many sequences of mixed lengths --------------------------
+
+@pytest.mark.parametrize("batch", [64, 65])
+@pytest.mark.parametrize("mask", ["none", "causal", "right_window"])
+def test_tile_order_many_sequences(fmha, oracle, batch, mask):
+    # causal or a right-only window: 64 sequences take the longest-first tile
+    # order, 65 the grouped one (as does no mask); the lengths mix empty
+    # sequences, q > k and k > q (rows before the first key)
+    rng = np.random.default_rng(batch)
+    choices = [0, 1, 31, 32, 33, 95, 128, 129, 200, 257, 300]
+    lens_q = [int(x) for x in rng.choice(choices, size=batch)]
+    lens_k = [int(x) for x in rng.choice(choices, size=batch)]
+    lens_q[0], lens_k[0] = 300, 300
+    prob = make_problem(f"tile_order_b{batch}", dtype="bf16" if mask == "none" else "f16",
+                        lens_q=lens_q, lens_k=lens_k, hq=8, hkv=2, dqk=128, dv=128,
+                        seed=11, varlen_q=True, varlen_k=True, causal=(mask == "causal"),
+                        window=(-1, 40) if mask == "right_window" else (-1, -1))
+    dev = upload(prob)
+    pl = fmha.plan(fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                                  cu_seqlens_k=dev["cu_seqlens_k"],
+                                  max_seqlen_q=dev["max_seqlen_q"],
+                                  max_seqlen_k=dev["max_seqlen_k"], causal=prob.causal,
+                                  window=prob.window, num_kv_splits=1))
+    assert pl.tile_order == (1 if batch <= 64 and mask != "none" else 0)
+    check(fmha, oracle, prob, splits=(1,), label=mask)
 
 
 # ---- edge set: lengths [1,0,63,64,65,128,129,700], GQA 8:2, bf16 ----------

@@ -249,3 +249,34 @@ def test_combine_rejections():
     assert fmha.lib.fmha_splitkv_combine(ctypes.byref(c), None) == INVALID
     c.split_chunk, c.out_dtype = 32, 3
     assert fmha.lib.fmha_splitkv_combine(ctypes.byref(c), None) == INVALID
+
+
+def test_tile_order_and_grid():
+    # 32-row-tile prefill, one split, causal or a right-only window, <= 64
+    # sequences: all tiles longest first, the grid bounded by the packed query
+    # count
+    lens = [4096, 512, 3072, 1024, 2560, 1536, 2048, 1536]
+    for kw in (dict(causal=True), dict(window=(-1, 0)), dict(window=(-1, 300))):
+        st, p = check(make(dtype=1, batch=8, sq=4096, sk=4096, hq=16, hkv=16, dqk=128,
+                           dv=128, varlen_q=True, varlen_k=True, total_q=sum(lens),
+                           total_k=sum(lens), splits=1, **kw))
+        assert st == OK and p.tile_order == 1 and p.rows_per_tile == 128, kw
+        # sum over sequences of ceil(len / 128) <= (16384 + 8 * 127) // 128 = 135 < 8 * 32
+        assert p.grid_main == 16 * 135
+    # fixed length: exact tile count
+    st, p = check(make(dtype=1, batch=8, sq=2048, sk=2048, hq=16, hkv=16, dqk=128, dv=128,
+                       causal=True, splits=1))
+    assert st == OK and p.tile_order == 1 and p.grid_main == 16 * 8 * 16
+    # no mask, a left window, more than 64 sequences, a split, or a decode
+    # shape: grouped
+    for kw in (dict(causal=False), dict(window=(128, 0)), dict(batch=65),
+               dict(splits=2, workspace=FAKE, workspace_bytes=1 << 40)):
+        args = dict(dtype=1, batch=8, sq=512, sk=512, hq=16, hkv=16, dqk=128, dv=128,
+                    splits=1, causal=True)
+        args.update(kw)
+        st, p = check(make(**args))
+        assert st == OK and p.tile_order == 0, kw
+        assert p.grid_main == args["batch"] * 16 * p.num_q_tiles * p.num_splits
+    st, p = check(make(dtype=1, batch=2, sq=1, sk=4096, hq=16, hkv=16, dqk=128, dv=128,
+                       splits=1, causal=True))
+    assert st == OK and p.tile_order == 0
