@@ -90,6 +90,14 @@ def workloads():
                                      fs.VARLEN_EQUAL, 16, 16, 128, 128, causal=True,
                                      varlen_q=True, varlen_k=True, seed=4,
                                      desc="varlen prefill fp16 H=16 D=128 8x2048 causal"),
+        # head dim 256 (the same flops per token with half the heads)
+        "varlen_equal_d256": _spec("varlen_equal_d256", "f16", fs.VARLEN_EQUAL, fs.VARLEN_EQUAL,
+                                   8, 8, 256, 256, varlen_q=True, varlen_k=True, seed=4,
+                                   desc="varlen prefill fp16 H=8 D=256 8x2048"),
+        "varlen_equal_causal_d256": _spec("varlen_equal_causal_d256", "f16", fs.VARLEN_EQUAL,
+                                          fs.VARLEN_EQUAL, 8, 8, 256, 256, causal=True,
+                                          varlen_q=True, varlen_k=True, seed=4,
+                                          desc="varlen prefill fp16 H=8 D=256 8x2048 causal"),
     }
 
 
@@ -480,7 +488,8 @@ def main():
     others = []
     if not args.no_others:
         for name in ("gqa_decode", "fp8_prefix_16384", "fp8_prefix_11008", "varlen_skewed",
-                     "varlen_skewed_causal", "varlen_equal", "varlen_equal_causal"):
+                     "varlen_skewed_causal", "varlen_equal", "varlen_equal_causal",
+                     "varlen_equal_d256", "varlen_equal_causal_d256"):
             if name == w["name"]:
                 continue
             o = W[name]

@@ -55,6 +55,7 @@ const FwdKernel* registry_bf16_decode(int* n) {
 static const FwdKernel kPfTable[] = {
     FMHA_PF(64, 4, 64, 200),
     FMHA_PF(128, 4, 32, 201),
+    FMHA_PF(256, 4, 32, 202),
 };
 
 const FwdKernel* registry_bf16_prefill(int* n) {

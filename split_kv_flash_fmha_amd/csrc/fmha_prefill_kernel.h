@@ -90,7 +90,9 @@ struct PfCfg {
   static constexpr int KL = TILE / 1024 / NWM;     // 1 KiB loads per wave per K (or V) block
   static constexpr int NS = 4;                     // ring depth, K and V each
   static constexpr int LDS = 2 * NS * TILE;
-  static constexpr int MIN_BLOCKS = (RT == 1 ? 8 : 4) / NWM;  // two waves per SIMD (one for RT = 2)
+  // two waves per SIMD (one for RT = 2, or when two rings do not fit the
+  // 160 KiB of LDS: D = 256 runs one wave per SIMD with all 512 registers)
+  static constexpr int MIN_BLOCKS = 2 * LDS > 160 * 1024 ? 1 : (RT == 1 ? 8 : 4) / NWM;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
   static_assert(1024 % ROWB == 0 && KL >= 1 && KL * NWM * 1024 == TILE, "whole 1 KiB loads per wave");
   static_assert(TILE % 256 == 0, "stage offsets keep the low address bits");
@@ -330,7 +332,8 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   // K fragment read addresses: k-step k of tile u (row 32u + lr) sits at
   // (kaddr[u] ^ 32k) within a stage (the swizzle only touches bits 5..7); the
   // stage offset is an immediate
-  static_assert(C::ROWB == 256 || C::ROWB == 128, "swizzles");
+  // (512-byte rows: the same XORs; the k-step and row fields stay disjoint)
+  static_assert(C::ROWB == 512 || C::ROWB == 256 || C::ROWB == 128, "swizzles");
   uint32_t kx[C::NT][C::KS];
 #pragma unroll
   for (int u = 0; u < C::NT; ++u) {
@@ -384,24 +387,27 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
 
   // O^T += V^T P^T for one key block from V stage VST with P from pb.  Lane
   // 4e+jq of 16-lane group (hl, grp) reads row 16g+8q+4hl+e, columns
-  // 32t+16grp+4jq..+3, and receives column lr of those 4 rows.  All fragments
-  // of the block are read up front (two reads per fragment n = (group g,
-  // tile t)); fragment n feeds one MFMA per row tile, which wait only for
-  // its own two reads; `between(n)` is VALU work placed after fragment n's
-  // MFMAs.
+  // 32t+16grp+4jq..+3, and receives column lr of those 4 rows.  Fragment n =
+  // (group g, tile t) takes two reads, issued up to PA fragments ahead (all
+  // of them up front when NM <= PA + 1); it feeds one MFMA per row tile, which
+  // waits only for its own two reads; `between(n)` is VALU work placed after
+  // fragment n's MFMAs.
   auto pv = [&](auto VST_, const u32x4 (&pb)[RT][C::NG], auto&& between) {
     constexpr int VST = decltype(VST_)::value;
     constexpr int NM = C::NG * C::TV;
-    static_assert(2 * NM - 2 <= 15, "lgkmcnt range");
+    constexpr int PA = 7;  // fragments in flight beyond the one consumed: lgkmcnt <= 14
     i32x2 vr[NM][2];
-    static_for<NM>([&](auto N_) {
+    auto read_v = [&](auto N_) {
       constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
       vr[n][0] = lds_tr16<VST * C::TILE + (16 * g) * C::ROWB>(vx[t]);
       vr[n][1] = lds_tr16<VST * C::TILE + (16 * g + 8) * C::ROWB>(vx[t]);
-    });
+    };
+    static_for<(NM < PA + 1 ? NM : PA + 1)>([&](auto N_) { read_v(N_); });
     static_for<NM>([&](auto N_) {
       constexpr int n = decltype(N_)::value, g = n / C::TV, t = n % C::TV;
-      lgkm_wait<2 * (NM - 1 - n)>();
+      if constexpr (n > 0 && n + PA < NM) read_v(int_c<n + PA>{});
+      // fragments issued after n: min(PA, NM - 1 - n), two reads each
+      lgkm_wait<2 * (NM - 1 - n < PA ? NM - 1 - n : PA)>();
       tie(vr[n][0]);
       tie(vr[n][1]);
       const u32x4 vf = {(uint32_t)vr[n][0].x, (uint32_t)vr[n][0].y, (uint32_t)vr[n][1].x, (uint32_t)vr[n][1].y};

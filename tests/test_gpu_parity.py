@@ -101,6 +101,17 @@ def test_varlen_prefill_small(fmha, oracle, lengths, causal):
     check(fmha, oracle, prob, splits=(0,))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_d256(fmha, oracle, dtype, causal):
+    # head dim 256 (one wave per SIMD, 512-byte K/V rows): skewed lengths over
+    # several 128-row tiles and 32-key blocks, ragged tails, GQA 8:2
+    lens = [300, 33, 129, 1, 257]
+    prob = make_problem("prefill_d256", dtype=dtype, lens_q=lens, lens_k=lens, hq=8, hkv=2,
+                        dqk=256, dv=256, seed=12, varlen_q=True, varlen_k=True, causal=causal)
+    check(fmha, oracle, prob, splits=(1,))
+
+
 def sample_rows(prob, n_random=384, seed=0):
     """Token/head pairs: first, last and tile-edge rows of every sequence + random."""
     rng = np.random.default_rng(seed)
