@@ -101,6 +101,16 @@ def test_varlen_prefill_small(fmha, oracle, lengths, causal):
     check(fmha, oracle, prob, splits=(0,))
 
 
+@pytest.mark.parametrize("sq,sk", [(300, 200), (200, 500), (257, 257)])
+def test_fixed_length_causal_prefill(fmha, oracle, sq, sk):
+    # fixed-length (batched, no cu_seqlens) causal prefill in the longest-first
+    # tile order; q > k leaves rows before the first key (O = 0, LSE = -inf)
+    prob = make_problem("fixed_causal", dtype="bf16", lens_q=[sq] * 3, lens_k=[sk] * 3, hq=8,
+                        hkv=4, dqk=128, dv=128, seed=13, varlen_q=False, varlen_k=False,
+                        causal=True)
+    check(fmha, oracle, prob, splits=(1, 0), label=f"{sq}x{sk}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_prefill_d256(fmha, oracle, dtype, causal):
