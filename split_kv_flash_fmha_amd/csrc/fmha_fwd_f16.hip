@@ -46,16 +46,12 @@ const FwdKernel* registry_f16_decode(int* n) {
 }
 
 // Prefill instances (32x32 MFMA tiles, 4 waves x 32 rows; key blocks of 32
-// keys for D = 128 and 64 keys for D = 64, 8 KiB of K or V per block).  Two
-// workgroups share a CU, so the two waves on a SIMD belong to different
-// workgroups and drift out of phase (one on MFMA while the other is on VALU).
+// keys for D = 128 and 256 and 64 keys for D = 64: 8 KiB of K or V per block,
+// 16 KiB for D = 256).  Two workgroups share a CU, so the two waves on a SIMD
+// belong to different workgroups and drift out of phase (one on MFMA while the
+// other is on VALU); D = 256 runs one workgroup per CU (its rings take 128 KiB).
 #define FMHA_PF(D, NWM, BN, ID) \
   {DT_F16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, NWM, BN, 1>>}
-
-// RT = 2: two waves x 64 rows (two 32-row tiles per wave: every K / V
-// fragment read from LDS feeds two MFMAs); `nwm` counts 32-row tiles.
-#define FMHA_PF2(D, NWM, BN, ID) \
-  {DT_F16, D, D, 2 * NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, NWM, BN, 2>>}
 
 static const FwdKernel kPfTable[] = {
     FMHA_PF(64, 4, 64, 200),

@@ -17,8 +17,9 @@
 // K and V blocks move HBM -> LDS with buffer loads that write LDS directly
 // (16 bytes per lane, no register staging), rows unpadded with an XOR chunk
 // swizzle that keeps both the 16-byte K reads and the V transpose reads free
-// of bank conflicts.  K and V each have a ring of three LDS stages; the loads
-// run two blocks ahead of their use, one barrier per block.
+// of bank conflicts.  K and V each have a ring of four LDS stages: iteration n
+// issues K(n+4) and V(n+2) and uses K(n+1) and V(n-1), so the loads of the
+// two previous iterations may still be in flight; one barrier per block.
 //
 // Software pipeline: iteration n runs PV(n-1) on the MFMA pipe while the VALU
 // takes the row max of block n, then QK(n+1) on the MFMA pipe while the VALU
