@@ -193,8 +193,9 @@ __device__ __forceinline__ WorkItem grouped_item(const FwdParams& p) {
 }
 
 // Inclusive prefix sum of v over the lanes of the wave: a scan within each
-// row of 16 lanes (DPP row shifts by 1, 2, 4, 8), then the last lane of row 0
-// (1) is added to rows 1 and 3 (2 and 3) by the row broadcasts.
+// row of 16 lanes (DPP row shifts by 1, 2, 4, 8); then row_bcast:15 adds the
+// last lane of rows 0 and 2 to rows 1 and 3, and row_bcast:31 adds lane 31
+// (the total of rows 0 and 1) to rows 2 and 3.
 __device__ __forceinline__ int wave_scan(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
   v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
