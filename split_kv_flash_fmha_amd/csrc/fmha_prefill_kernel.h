@@ -217,7 +217,7 @@ __device__ __forceinline__ float max_halves(float x) {
 // Read schedule of the interleaved PV/QK phase: reads are numbered in the
 // order MFMA j = 0, 1, ... (PV n = j / 2 for even j, QK n for odd j) needs
 // them, three per fragment pair (two V transpose reads, one K read).
-constexpr int kPvqkAhead = 9;  // reads issued beyond the ones the next MFMA needs
+constexpr int kPvqkAhead = 6;  // reads issued beyond the ones the next MFMA needs (3..15 timed: 6 best by ~1 %)
 // reads that must have completed before MFMA j
 constexpr int pvqk_need(int j) { return 3 * (j / 2) + (j % 2 ? 3 : 2); }
 // reads issued before MFMA j
