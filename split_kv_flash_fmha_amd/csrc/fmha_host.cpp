@@ -162,6 +162,22 @@ int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num
   int64_t s = (sk_max + chunk - 1) / chunk;
   if (s < 1) s = 1;
   if (s > FMHA_MAX_SPLITS) s = FMHA_MAX_SPLITS;
+  // Keys per split of s splits, as the launch cuts them.  A power-of-two
+  // number of key blocks per split starts every split's stream at the same
+  // offset modulo a large power of two of bytes (long decode: 1024 keys x
+  // 8 KiB rows, so the ~2048 concurrent wave streams are congruent mod
+  // 2 MiB); measured on MI355X, such chunks ran 6 % (long decode, 1024 keys)
+  // and 14 % (GQA decode, 512 keys) slower than the neighbouring sizes, so
+  // take fewer splits until the chunk is not one.
+  auto chunk_of = [&](int64_t n) {
+    const int64_t c = (sk_max + n - 1) / n;
+    return (c + sb - 1) / sb * sb;
+  };
+  auto pow2_blocks = [&](int64_t c) {
+    const int64_t nb = c / sb;
+    return nb >= 4 && (nb & (nb - 1)) == 0;
+  };
+  while (s > 1 && pow2_blocks(chunk_of(s))) --s;
   return (int)s;
 }
 

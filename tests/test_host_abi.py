@@ -202,6 +202,21 @@ def test_auto_splits_long_decode_fills_device():
     assert n.value * 32 >= 2 * 256
 
 
+def test_auto_splits_avoid_power_of_two_chunks():
+    # a power-of-two number of 32-key blocks per split aligns every split's
+    # stream (measured slower); the automatic count steps past such chunks
+    for sk, hq in ((131072, 32), (65536, 32), (16384, 8)):
+        st, p = check(make(sq=1, sk=sk, hq=hq, hkv=hq, dqk=128, dv=128, splits=0,
+                           workspace=FAKE, workspace_bytes=1 << 40))
+        assert st == OK and p.num_splits > 1
+        nb = p.split_chunk // p.key_block
+        assert not (nb >= 4 and nb & (nb - 1) == 0), (sk, p.num_splits, p.split_chunk)
+    # long decode: 127 splits of 1056 keys instead of 128 of 1024
+    st, p = check(make(sq=1, sk=131072, hq=32, hkv=32, dqk=128, dv=128, splits=0,
+                       workspace=FAKE, workspace_bytes=1 << 40))
+    assert (p.num_splits, p.split_chunk) == (127, 1056)
+
+
 def test_auto_splits_scale_with_cu_count():
     base = dict(sq=1, sk=131072, hq=32, hkv=32, dqk=128, dv=128)
     s = []
