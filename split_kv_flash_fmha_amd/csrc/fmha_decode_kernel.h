@@ -73,28 +73,21 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_decode_kernel(FwdParams p) {
   const int lr = lane & 15;
   char* Vs = smem + wk * C::BN * C::VP;  // this wave's V tile
 
-  int64_t bid = blockIdx.x;
   const int S = p.num_splits;
-  const int split = (int)(bid % S);
-  bid /= S;
-  const int hkv = (int)(bid % p.hkv);
-  const int b = (int)(bid / p.hkv);
-
-  int q_off, sq, k_off, sk;
-  if (p.cu_q) {
-    q_off = p.cu_q[b];
-    sq = p.cu_q[b + 1] - q_off;
+  WorkItem wi;
+  if (p.tile_order == kTileOrderFullFirst) {
+    if (!full_first_item(p, wi)) return;
   } else {
-    q_off = b * p.seqlen_q;
-    sq = p.seqlen_q;
+    // split fastest: the splits of one (sequence, kv head) on consecutive blocks
+    int64_t bid = blockIdx.x;
+    wi.split = (int)(bid % S);
+    bid /= S;
+    wi.hkv = (int)(bid % p.hkv);
+    wi.b = (int)(bid / p.hkv);
+    seq_span(p, wi.b, wi);
   }
-  if (p.cu_k) {
-    k_off = p.cu_k[b];
-    sk = p.cu_k[b + 1] - k_off;
-  } else {
-    k_off = b * p.seqlen_k;
-    sk = p.seqlen_k;
-  }
+  const int split = wi.split, hkv = wi.hkv, b = wi.b;
+  const int q_off = wi.q_off, sq = wi.sq, k_off = wi.k_off, sk = wi.sk;
   const int G = p.group;
   const int rows = sq * G;
   if (rows <= 0 || sk <= 0) return;

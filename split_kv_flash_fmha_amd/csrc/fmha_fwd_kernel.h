@@ -284,6 +284,64 @@ __device__ __forceinline__ bool longest_first_item(const FwdParams& p, WorkItem&
   return true;
 }
 
+// Full-first order (kTileOrderFullFirst): the decode kernel with more than one
+// split, at most 64 sequences (lane b of every wave holds sequence b).  With
+// splits of `chunk` keys, sequence b has nf_b = sk_b / chunk full splits and,
+// when sk_b is not a multiple of chunk, one partial split of the remaining
+// keys.  Positions [0, H * sum nf) hold the full splits in (sequence, kv head,
+// split) order -- the splits of one (sequence, kv head) on consecutive blocks,
+// which the hardware deals to different XCDs -- and the positions after them
+// the partial splits, longest first (ties: lower sequence first), the kv heads
+// of one sequence consecutive.  The 32 in-order dispatch lanes then end on the
+// shortest items instead of a mix of full and partial ones.  Positions past
+// the last split return false.
+__device__ __forceinline__ bool full_first_item(const FwdParams& p, WorkItem& w) {
+  const int lane = threadIdx.x & 63;
+  const bool real = lane < p.batch;
+  WorkItem sp;
+  seq_span(p, real ? lane : p.batch - 1, sp);  // clamped: every lane loads in bounds
+  const bool has = real && sp.sq > 0 && sp.sk > 0;
+  const int S = p.num_splits, chunk = p.chunk;
+  const int nf = has ? min(sp.sk / chunk, S) : 0;         // full splits
+  const int rem = has && nf < S ? sp.sk - nf * chunk : 0;  // keys of the partial split
+  const int H = p.hkv;
+  const int pos = blockIdx.x;
+  const int incl = wave_scan(nf);
+  const int nfull = H * __builtin_amdgcn_readlane(incl, 63);
+  int b, split;
+  if (pos < nfull) {
+    const int excl = incl - nf;
+    const uint64_t sel = __ballot(nf > 0 && H * excl <= pos && pos < H * incl);
+    if (sel == 0) return false;  // not reached: the ranges partition [0, nfull)
+    b = (int)__builtin_ctzll(sel);
+    const int j = pos - H * __builtin_amdgcn_readlane(excl, b);
+    const int f = __builtin_amdgcn_readlane(nf, b);
+    w.hkv = j / f;
+    split = j % f;
+  } else {
+    const int j = pos - nfull;
+    // rank of this sequence's partial split among all partial splits
+    int rank = 0;
+    for (int i = 0; i < p.batch; ++i) {
+      const int ri = __builtin_amdgcn_readlane(rem, i);
+      rank += (ri > rem || (ri == rem && i < lane)) ? 1 : 0;
+    }
+    const uint64_t sel = __ballot(rem > 0 && rank == j / H);
+    if (sel == 0) return false;  // past the last partial split
+    b = (int)__builtin_ctzll(sel);
+    w.hkv = j % H;
+    split = __builtin_amdgcn_readlane(nf, b);
+  }
+  w.split = split;
+  w.b = b;
+  w.qtile = 0;
+  w.q_off = __builtin_amdgcn_readlane(sp.q_off, b);
+  w.sq = __builtin_amdgcn_readlane(sp.sq, b);
+  w.k_off = __builtin_amdgcn_readlane(sp.k_off, b);
+  w.sk = __builtin_amdgcn_readlane(sp.sk, b);
+  return true;
+}
+
 // This workgroup's item; false: nothing to do.
 template <int ROWS>
 __device__ __forceinline__ bool work_item(const FwdParams& p, WorkItem& w) {

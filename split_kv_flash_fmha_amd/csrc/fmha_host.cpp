@@ -13,6 +13,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/fmha.h"
 #include "fmha_params.h"
 
@@ -136,16 +138,24 @@ struct Resolved {
 // range is cut into splits of at least kMinChunk keys.  The split sweeps on
 // the pages show time falling steeply until the grid covers the machine and
 // flattening or rising past that point.  On MI355X:
-//  * the decode kernel (2 resident workgroups per CU, one 16-row tile) keeps
-//    improving until each CU has seen ~16 workgroups, which also evens out
-//    sequences of different lengths;
+//  * the streaming kernels (2 resident workgroups per CU, one 16-row tile)
+//    keep improving until each CU has seen ~16 workgroups, which also evens
+//    out sequences of different lengths.  The decode kernel, whose splits are
+//    ordered full ones first, takes as few as 8 per CU where that gives
+//    splits of kDecodeChunk keys: each workgroup spends ~4.5 us on its
+//    prologue and merge, and with 544-key splits that was a quarter of its
+//    life (GQA decode, 16 x 8 kv heads, keys ~ U[1024, 32768]: 31 splits of
+//    1056 keys ran 4 % faster than 60 of 544 on three length draws; long
+//    decode, already at 1056 keys, is unchanged);
 //  * the multi-row (prefill-family) kernels hold a large LDS ring per
 //    workgroup and run fastest with exactly one wave of workgroups: splits
 //    are chosen so that units x splits just fits the CU count, since a
 //    second round of workgroups on a few CUs doubles the time.
-int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num_cus, bool one_round) {
+int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num_cus, bool one_round,
+                bool decode) {
   constexpr int kTargetPerCu = 16;
   constexpr int64_t kMinChunk = 256;
+  constexpr int64_t kDecodeChunk = 1024;
   if (sk_max <= 0) return 1;
   int64_t chunk;
   if (one_round) {
@@ -156,6 +166,10 @@ int auto_splits(int64_t units, int64_t key_work, int64_t sk_max, int sb, int num
     const int64_t target = (int64_t)kTargetPerCu * num_cus;
     if (units >= target / 2) return 1;
     chunk = (key_work + target - 1) / target;
+    if (decode) {
+      const int64_t half = target / 2;
+      chunk = std::max(chunk, std::min(kDecodeChunk, (key_work + half - 1) / half));
+    }
   }
   if (chunk < kMinChunk) chunk = kMinChunk;
   chunk = (chunk + sb - 1) / sb * sb;
@@ -282,7 +296,7 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     S = a->num_kv_splits;
   } else {
     const int64_t key_work = (int64_t)a->num_heads_kv * pl.num_q_tiles * r->total_k;
-    S = auto_splits(units, key_work, r->sk_max, pl.key_block, num_cus, prefill);
+    S = auto_splits(units, key_work, r->sk_max, pl.key_block, num_cus, prefill, kern->bn == 0);
   }
   pl.num_splits = S;
   if (S > 1) {
@@ -312,6 +326,11 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     const int64_t slots = (int64_t)a->batch * pl.num_q_tiles;
     pl.grid_main = (int64_t)a->num_heads_kv * (tiles < slots ? tiles : slots);
   }
+  // the decode kernel's splits: full ones first, then the partial ones longest
+  // first (the grid keeps its (sequence, kv head, split) size; positions past
+  // the last split return at once)
+  if (kern->bn == 0 && S > 1 && a->batch <= kLongestFirstMaxBatch && !r->empty)
+    pl.tile_order = kTileOrderFullFirst;
   if (pl.grid_main >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
   pl.grid_combine = (r->empty || S == 1) ? 0 : combine_grid(a->head_dim_v, S, r->sq_max * a->num_heads_q * a->batch);
   if (pl.grid_combine >= kMaxGrid) return FMHA_ERR_INVALID_ARG;

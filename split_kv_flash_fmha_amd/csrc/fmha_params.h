@@ -47,6 +47,7 @@ struct FwdParams {
 // Block -> tile orders of the attention launch.
 constexpr int32_t kTileOrderGrouped = 0;       // by (sequence, kv head), XCD-grouped
 constexpr int32_t kTileOrderLongestFirst = 1;  // all tiles by cost, longest first
+constexpr int32_t kTileOrderFullFirst = 2;     // decode splits: full ones, then partial ones by length
 constexpr int kLongestFirstMaxBatch = 64;      // one sequence per lane of a wave
 
 struct CombineParams {

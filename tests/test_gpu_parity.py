@@ -189,6 +189,29 @@ def test_tile_order_many_sequences(fmha, oracle, batch, mask):
     check(fmha, oracle, prob, splits=(1,), label=mask)
 
 
+@pytest.mark.parametrize("batch", [64, 65])
+def test_decode_split_order_many_sequences(fmha, oracle, batch):
+    # decode with splits: 64 sequences take the full-first split order, 65 the
+    # plain one; the key lengths mix empty sequences, exact multiples of the
+    # 96-key chunk (7 splits of max 672 keys) and partial last splits, the query
+    # lengths 0..4 rows per sequence (GQA 4:1 packs them into one 16-row tile)
+    rng = np.random.default_rng(100 + batch)
+    lens_q = [int(x) for x in rng.choice([0, 1, 1, 1, 2, 4], size=batch)]
+    lens_k = [int(x) for x in rng.choice([0, 1, 31, 96, 97, 192, 300, 480, 671, 672], size=batch)]
+    lens_q[0], lens_k[0] = 1, 672
+    prob = make_problem(f"decode_order_b{batch}", dtype="bf16", lens_q=lens_q, lens_k=lens_k,
+                        hq=8, hkv=2, dqk=128, dv=128, seed=12, varlen_q=True, varlen_k=True)
+    dev = upload(prob)
+    pl = fmha.plan(fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                                  cu_seqlens_k=dev["cu_seqlens_k"],
+                                  max_seqlen_q=dev["max_seqlen_q"],
+                                  max_seqlen_k=dev["max_seqlen_k"], num_kv_splits=7,
+                                  workspace=torch.empty(16 << 20, dtype=torch.uint8,
+                                                        device="cuda")))
+    assert pl.split_chunk == 96 and pl.tile_order == (2 if batch <= 64 else 0)
+    check(fmha, oracle, prob, splits=(7, 0), label=f"decode order b{batch}")
+
+
 # ---- edge set: lengths [1,0,63,64,65,128,129,700], GQA 8:2, bf16 ----------
 
 @pytest.mark.parametrize("mask", ["window", "none", "causal"])

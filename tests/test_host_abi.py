@@ -217,6 +217,24 @@ def test_auto_splits_avoid_power_of_two_chunks():
     assert (p.num_splits, p.split_chunk) == (127, 1056)
 
 
+def test_auto_splits_decode_prefers_long_splits():
+    # batched GQA decode (16 x 8 kv heads, keys ~ U[1024, 32768]): splits of
+    # ~1024 keys while each CU still sees >= 8 workgroups -- 31 splits of 1056
+    # keys (1024 is a power-of-two block count), not 60 of 544
+    st, p = check(make(batch=16, sq=1, sk=32542, hq=32, hkv=8, dqk=128, dv=128, varlen_k=True,
+                       total_k=266241, splits=0, workspace=FAKE, workspace_bytes=1 << 40))
+    assert st == OK and (p.num_splits, p.split_chunk) == (31, 1056)
+    # too little work for 8 per CU at 1024 keys: the chunk shrinks with it
+    st, p = check(make(batch=1, sq=1, sk=65536, hq=8, hkv=8, dqk=128, dv=128, splits=0,
+                       workspace=FAKE, workspace_bytes=1 << 40))
+    assert st == OK and p.split_chunk < 1024 and p.num_splits * 8 >= 8 * 256 // 2
+    # the same shape through the 16-row streaming kernel (fp32): 16 per CU
+    st, p = check(make(dtype=0, batch=16, sq=1, sk=32542, hq=32, hkv=8, dqk=128, dv=128,
+                       varlen_k=True, total_k=266241, splits=0, workspace=FAKE,
+                       workspace_bytes=1 << 40))
+    assert st == OK and p.split_chunk < 1024
+
+
 def test_auto_splits_scale_with_cu_count():
     base = dict(sq=1, sk=131072, hq=32, hkv=32, dqk=128, dv=128)
     s = []
@@ -295,3 +313,23 @@ def test_tile_order_and_grid():
     st, p = check(make(dtype=1, batch=2, sq=1, sk=4096, hq=16, hkv=16, dqk=128, dv=128,
                        splits=1, causal=True))
     assert st == OK and p.tile_order == 0
+
+
+def test_decode_split_order():
+    # the decode kernel with more than one split and <= 64 sequences: full
+    # splits first, then the partial ones (order 2); the grid keeps its
+    # (sequence, kv head, split) size
+    for dtype in (1, 2, 3):
+        for batch in (1, 16, 64):
+            st, p = check(make(dtype=dtype, batch=batch, sq=1, sk=20000, hq=32, hkv=8, dqk=128,
+                               dv=128, varlen_k=True, total_k=max(20000, batch * 9000), splits=0,
+                               workspace=FAKE, workspace_bytes=1 << 40))
+            assert st == OK and p.num_splits > 1 and p.tile_order == 2, (dtype, batch)
+            assert p.grid_main == batch * 8 * p.num_splits
+    # 65 sequences, one split, or fp32 (no decode kernel): the plain order
+    for kw in (dict(batch=65), dict(splits=1), dict(dtype=0)):
+        args = dict(dtype=2, batch=16, sq=1, sk=20000, hq=32, hkv=8, dqk=128, dv=128,
+                    varlen_k=True, splits=4, workspace=FAKE, workspace_bytes=1 << 40)
+        args.update(kw)
+        st, p = check(make(**args))
+        assert st == OK and p.tile_order == 0, kw
