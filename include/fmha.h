@@ -195,7 +195,9 @@ typedef struct fmha_fwd_plan {
   size_t lse_part_offset;
   int32_t tile_order;   /* 0: tiles grouped by (sequence, kv head); 1: all tiles
                            longest first (32-row-tile prefill kernels, one split,
-                           causal or a right-only window, batch <= 64) */
+                           causal or a right-only window, batch <= 64); 2: decode
+                           splits, full ones first, then the partial ones longest
+                           first (decode kernel, more than one split, batch <= 64) */
 } fmha_fwd_plan;
 
 /*
