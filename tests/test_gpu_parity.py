@@ -86,6 +86,16 @@ def test_fp8_prefix_causal_split(fmha, oracle):
     check(fmha, oracle, prob, splits=(4, 1, 0), label="causal")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_varlen_prefix(fmha, oracle, causal):
+    # packed fp8 (Dqk=192, Dv=128) with key offsets that are not multiples of
+    # 16 (the unaligned varlen case) and query counts around the 32-row tiles
+    prob = make_problem("fp8_varlen", dtype="fp8_e4m3", lens_q=[70, 17, 33, 96, 1],
+                        lens_k=[1000, 77, 1301, 515, 9], hq=12, hkv=4, dqk=192, dv=128,
+                        seed=13, varlen_q=True, varlen_k=True, causal=causal)
+    check(fmha, oracle, prob, splits=(0, 1, 3), label=f"causal={causal}")
+
+
 # ---- varlen prefill ------------------------------------------------------
 
 SMALL_SKEWED = [256, 32, 192, 64, 160, 96, 128, 96]
