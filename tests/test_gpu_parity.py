@@ -222,6 +222,28 @@ def test_decode_split_order_many_sequences(fmha, oracle, batch):
     check(fmha, oracle, prob, splits=(7, 0), label=f"decode order b{batch}")
 
 
+@pytest.mark.parametrize("dtype,d,dv", [("f16", 64, 64), ("f16", 128, 128), ("bf16", 64, 64),
+                                        ("fp8_e4m3", 128, 128), ("fp8_e4m3", 192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_kernels(fmha, oracle, dtype, d, dv, causal):
+    # every decode instance (<= 16 rows per (sequence, kv head): 1..4 queries x
+    # 4 q heads per kv head), packed keys of mixed lengths including an empty
+    # sequence and one shorter than its queries
+    prob = make_problem(f"decode_{dtype}_{d}", dtype=dtype, lens_q=[1, 4, 2, 1, 3],
+                        lens_k=[3000, 517, 0, 33, 2], hq=8, hkv=2, dqk=d, dv=dv, seed=14,
+                        varlen_q=True, varlen_k=True, causal=causal)
+    dev = upload(prob)
+    pl = fmha.plan(fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                                  cu_seqlens_k=dev["cu_seqlens_k"],
+                                  max_seqlen_q=dev["max_seqlen_q"],
+                                  max_seqlen_k=dev["max_seqlen_k"], causal=causal,
+                                  num_kv_splits=1, q_descale=dev.get("q_descale"),
+                                  k_descale=dev.get("k_descale"),
+                                  v_descale=dev.get("v_descale")))
+    assert pl.kernel_id % 1000 in (100, 101), pl.kernel_id  # a decode instance
+    check(fmha, oracle, prob, splits=(0, 1, 5), label=f"causal={causal}")
+
+
 # ---- edge set: lengths [1,0,63,64,65,128,129,700], GQA 8:2, bf16 ----------
 
 @pytest.mark.parametrize("mask", ["window", "none", "causal"])
