@@ -86,14 +86,26 @@ def test_fp8_prefix_causal_split(fmha, oracle):
     check(fmha, oracle, prob, splits=(4, 1, 0), label="causal")
 
 
+@pytest.mark.parametrize("dqk,lens_q", [(192, [70, 17, 33, 96, 1]), (192, [20, 5, 31, 1, 9]),
+                                         (128, [70, 17, 33, 96, 1]), (128, [20, 5, 31, 1, 9])])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_varlen_prefix(fmha, oracle, causal):
-    # packed fp8 (Dqk=192, Dv=128) with key offsets that are not multiples of
-    # 16 (the unaligned varlen case) and query counts around the 32-row tiles
-    prob = make_problem("fp8_varlen", dtype="fp8_e4m3", lens_q=[70, 17, 33, 96, 1],
-                        lens_k=[1000, 77, 1301, 515, 9], hq=12, hkv=4, dqk=192, dv=128,
+def test_fp8_varlen_prefix(fmha, oracle, dqk, lens_q, causal):
+    # packed fp8 (Dv=128) with key offsets that are not multiples of 16 (the
+    # unaligned varlen case) and query counts around the 32-row tiles; GQA 3:1
+    # gives at most 288 rows (the 128-row kernel) or 93 (the 96-row one)
+    prob = make_problem("fp8_varlen", dtype="fp8_e4m3", lens_q=lens_q,
+                        lens_k=[1000, 77, 1301, 515, 9], hq=12, hkv=4, dqk=dqk, dv=128,
                         seed=13, varlen_q=True, varlen_k=True, causal=causal)
-    check(fmha, oracle, prob, splits=(0, 1, 3), label=f"causal={causal}")
+    dev = upload(prob)
+    pl = fmha.plan(fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                                  cu_seqlens_k=dev["cu_seqlens_k"],
+                                  max_seqlen_q=dev["max_seqlen_q"],
+                                  max_seqlen_k=dev["max_seqlen_k"], causal=causal,
+                                  num_kv_splits=1, q_descale=dev.get("q_descale"),
+                                  k_descale=dev.get("k_descale"),
+                                  v_descale=dev.get("v_descale")))
+    assert pl.rows_per_tile == (128 if max(lens_q) * 3 > 96 else 96), pl.rows_per_tile
+    check(fmha, oracle, prob, splits=(0, 1, 3), label=f"d={dqk} causal={causal}")
 
 
 # ---- varlen prefill ------------------------------------------------------
