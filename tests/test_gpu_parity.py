@@ -256,6 +256,30 @@ def test_decode_kernels(fmha, oracle, dtype, d, dv, causal):
     check(fmha, oracle, prob, splits=(0, 1, 5), label=f"causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("max_q,nwm", [(1, 1), (6, 2), (12, 4), (20, 5)])
+def test_generic_kernel_tiles(fmha, oracle, dtype, d, max_q, nwm):
+    # the 16-row-tile kernel at each of its tile heights: GQA 4:1 packs
+    # max_q queries into 4 * max_q rows (f16/bf16 use it from 17 to 80 rows and,
+    # for head dims without a decode instance, below; f32 throughout)
+    if dtype != "f32" and nwm == 1 and d != 256:
+        pytest.skip("served by the decode kernel")
+    if dtype == "f32" and d == 256:
+        pytest.skip("no f32 instance at D = 256 (UNSUPPORTED)")
+    prob = make_problem(f"generic_{dtype}_{d}_{max_q}", dtype=dtype, lens_q=[max_q, max_q // 2 + 1, 1],
+                        lens_k=[300, 77, 40], hq=8, hkv=2, dqk=d, dv=d, seed=15, varlen_q=True,
+                        varlen_k=True, causal=True)
+    dev = upload(prob)
+    pl = fmha.plan(fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                                  cu_seqlens_k=dev["cu_seqlens_k"],
+                                  max_seqlen_q=dev["max_seqlen_q"],
+                                  max_seqlen_k=dev["max_seqlen_k"], causal=True,
+                                  num_kv_splits=1))
+    assert pl.rows_per_tile == 16 * nwm, pl.rows_per_tile
+    check(fmha, oracle, prob, splits=(0, 1, 3), label=f"nwm={nwm}")
+
+
 # ---- edge set: lengths [1,0,63,64,65,128,129,700], GQA 8:2, bf16 ----------
 
 @pytest.mark.parametrize("mask", ["window", "none", "causal"])
