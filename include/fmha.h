@@ -272,6 +272,24 @@ int fmha_splitkv_combine(const fmha_combine_args* args, void* stream);
 /* Human-readable name of a status code (static string). */
 const char* fmha_status_str(int status);
 
+/*
+ * Check a cumulative sequence-length array on the device against the
+ * contract above ("Adds variable sequence lengths to the Hopper CuTe DSL FMHA
+ * example", section Interface): cu_seqlens[0] == 0, non-decreasing,
+ * cu_seqlens[batch] == total, and no sequence longer than max_seqlen.  Enqueues one single-workgroup kernel on `stream` that reads
+ * cu_seqlens[0..batch] (caller-owned device memory, batch + 1 int32) and
+ * writes one int32 to `result` (caller-owned device memory): 0 if the array
+ * meets the contract, else 1 + the smallest index b at which it fails (b == 0:
+ * a non-zero first entry; b in 1..batch: a decrease or a sequence longer than
+ * max_seqlen ending at b; b == batch also: a last entry other than total).
+ * A debug aid for arrays that come from elsewhere: the forward calls never
+ * read cu_seqlens on the host.  Returns FMHA_ERR_INVALID_ARG (nothing
+ * enqueued) for a NULL pointer or a negative batch, total or max_seqlen,
+ * FMHA_ERR_HIP if the launch fails.
+ */
+int fmha_check_seqlens(const int32_t* cu_seqlens, int32_t batch, int32_t total, int32_t max_seqlen,
+                       int32_t* result, void* stream);
+
 /* Compute units of the current HIP device (a HIP query; FMHA_ERR_HIP on failure). */
 int fmha_device_num_cus(int32_t* num_cus_out);
 

@@ -107,9 +107,10 @@ def _load():
     L.fmha_status_str.argtypes = [ctypes.c_int]
     L.fmha_status_str.restype = ctypes.c_char_p
     L.fmha_device_num_cus.argtypes = [P(_i32)]
+    L.fmha_check_seqlens.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp]
     for f in ("fmha_fwd_check", "fmha_num_splits", "fmha_fwd_workspace_size",
               "fmha_fwd", "fmha_fwd_splitkv_partials", "fmha_splitkv_combine",
-              "fmha_device_num_cus"):
+              "fmha_device_num_cus", "fmha_check_seqlens"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -134,6 +135,20 @@ def device_num_cus() -> int:
         _raise(lib.fmha_device_num_cus(ctypes.byref(n)), "fmha_device_num_cus")
         _NUM_CUS[dev] = int(n.value)
     return _NUM_CUS[dev]
+
+
+def check_seqlens(cu_seqlens, total: int, max_seqlen: int) -> int:
+    """fmha_check_seqlens: check a device cu_seqlens array (int32, batch + 1
+    entries) against the varlen contract.  Returns 0 if it holds, else 1 + the
+    first failing index.  Synchronises the current stream to read the result."""
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+    cu = cu_seqlens.contiguous()
+    res = torch.empty(1, dtype=torch.int32, device=cu.device)
+    stream = torch.cuda.current_stream(cu.device).cuda_stream
+    _raise(lib.fmha_check_seqlens(cu.data_ptr(), cu.numel() - 1, int(total), int(max_seqlen),
+                                  res.data_ptr(), stream), "fmha_check_seqlens")
+    return int(res.item())
 
 
 def _ptr(t):

@@ -541,6 +541,14 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
   return FMHA_OK;
 }
 
+int fmha_check_seqlens(const int32_t* cu_seqlens, int32_t batch, int32_t total, int32_t max_seqlen,
+                       int32_t* result, void* stream) {
+  if (!cu_seqlens || !result || batch < 0 || total < 0 || max_seqlen < 0) return FMHA_ERR_INVALID_ARG;
+  if (fmha::launch_check_seqlens(cu_seqlens, batch, total, max_seqlen, result, (hipStream_t)stream) != hipSuccess)
+    return FMHA_ERR_HIP;
+  return FMHA_OK;
+}
+
 int fmha_device_num_cus(int32_t* num_cus_out) {
   if (!num_cus_out) return FMHA_ERR_INVALID_ARG;
   int dev = 0, n = 0;

@@ -116,5 +116,7 @@ inline int64_t combine_grid(int dv, int num_splits, int64_t rows) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_check_seqlens(const int32_t* cu, int32_t batch, int32_t total, int32_t max_seqlen,
+                                int32_t* result, hipStream_t stream);
 
 }  // namespace fmha

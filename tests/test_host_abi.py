@@ -33,6 +33,15 @@ def test_header_symbols_exported():
         assert hasattr(fmha.lib, n), f"{n} declared in include/fmha.h but not exported"
 
 
+def test_check_seqlens_argument_errors():
+    # rejected on the host before any launch (no GPU needed)
+    f = fmha.lib.fmha_check_seqlens
+    assert f(None, 2, 10, 10, FAKE, None) == INVALID
+    assert f(FAKE, 2, 10, 10, None, None) == INVALID
+    for batch, total, mx in ((-1, 0, 0), (1, -1, 0), (1, 0, -1)):
+        assert f(FAKE, batch, total, mx, FAKE, None) == INVALID
+
+
 def make(*, dtype=2, out_dtype=None, batch=1, sq=1, sk=1024, hq=4, hkv=4, dqk=64, dv=64,
          varlen_q=False, varlen_k=False, max_q=None, max_k=None, total_q=None, total_k=None,
          scale=0.0, causal=False, window=(-1, -1), splits=1, num_cus=256, lse=True,
