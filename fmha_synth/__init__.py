@@ -123,8 +123,13 @@ class Problem:
 
 def make_problem(name, *, dtype, lens_q, lens_k, hq, hkv, dqk, dv, seed,
                  varlen_q=None, varlen_k=None, causal=False, window=(-1, -1),
-                 device="cpu") -> Problem:
-    """Draw Q, K, V for the given per-sequence lengths (packed along tokens)."""
+                 device="cpu", shape_draws=None) -> Problem:
+    """Draw Q, K, V for the given per-sequence lengths (packed along tokens).
+
+    ``shape_draws(q32, k32, v32)``, when given, may overwrite the fp32 draws in
+    place before the cast (a caller-supplied input structure, e.g. keys placed
+    at chosen score heights by a test); this module computes nothing with it.
+    """
     lens_q = [int(x) for x in lens_q]
     lens_k = [int(x) for x in lens_k]
     if varlen_q is None:
@@ -137,6 +142,8 @@ def make_problem(name, *, dtype, lens_q, lens_k, hq, hkv, dqk, dv, seed,
     q32 = randn(gen, (tq, hq, dqk), device)
     k32 = randn(gen, (tk, hkv, dqk), device)
     v32 = randn(gen, (tk, hkv, dv), device)
+    if shape_draws is not None:
+        shape_draws(q32, k32, v32)
     q, qd = cast(q32, dtype)
     del q32
     k, kd = cast(k32, dtype)

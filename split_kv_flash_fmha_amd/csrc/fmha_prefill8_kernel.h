@@ -10,12 +10,11 @@
 //  * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 (64 d per MFMA): lane half h
 //    of d chunk c carries d = 64c + 32h + b in byte b, for K (two 16-byte LDS
 //    reads) and for Q (held in registers) alike.
-//  * K and V blocks sit in LDS "chunk-major": 16-byte column c of all BN rows
-//    is contiguous (BN rows x 16 bytes), which suits any row length (192-byte
-//    K rows) and makes each 1 KiB buffer->LDS load one column of 64 rows.  The
-//    16-byte K reads of 16 consecutive rows are contiguous; V columns are
-//    padded by 64 bytes so the two columns of one transpose-read pass fall in
-//    different banks.
+//  * K and V blocks sit in LDS row-major, filled by 1 KiB buffer->LDS loads
+//    whose 64 lanes fetch whole rows from HBM: K rows with one 16-byte pad
+//    slot per row (pitch Dqk + 16), V rows unpadded with their 16-byte chunks
+//    XOR-swizzled, both free of bank conflicts for the MFMA-operand and
+//    transpose reads.
 //  * O^T += V^T P^T on the same MFMA (64 keys per MFMA): byte 16u+4j+i of
 //    lane half h carries key 32u+8j+4h+i, which is where the S^T output puts
 //    that key, so P^T is packed straight from it; V^T comes from four
@@ -24,6 +23,12 @@
 //    factor 8 is carried by l as well (it cancels in O and is taken out of the
 //    LSE); a row's 32 stored values sum to at most 448 unless the check sends
 //    the block to the slow path, so each stays inside e4m3's range.
+//  * Two row sums: l of the fp32 p (for the LSE) and lq of the e4m3 P that
+//    the PV MFMA actually multiplies (for O = acc / lq).  With 3 mantissa
+//    bits a single P can be off by 6 %; normalising by the rounded weights
+//    keeps O a convex combination of V rows, so a row dominated by a few keys
+//    does not carry their rounding times |v|.  lq comes from the MFMA pipe:
+//    one 16x16x128 MFMA per block whose B operand is the block's P^T.
 //  * Rings of LA + 2 K and V stages in LDS: the loads of LA key blocks are in
 //    flight while a block is computed.
 #pragma once
@@ -46,12 +51,21 @@ __device__ __forceinline__ f32x16 mfma64_fp8(f32x16 acc, u32x8 a, u32x8 b) {
                                                          acc, 0, 0, 0, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x128_f8f6f4 with e4m3 A and B.  Operand lane l: row (A) /
+// column (B) l % 16, k-group l / 16 (its 32 bytes, byte b of A pairing with
+// byte b of B); output lane l: column l % 16, rows 4 (l / 16) + i in
+// register i.
+__device__ __forceinline__ f32x4 mfma128_fp8(f32x4 acc, u32x8 a, u32x8 b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                          acc, 0, 0, 0, 0, 0, 0);
+}
+
 template <int DQK_, int DV_, int NWM_, int LA_>
 struct Pf8Cfg {
   static constexpr int DQK = DQK_;
   static constexpr int DV = DV_;
   static constexpr int NWM = NWM_;
-  static constexpr int BN = 64;          // keys per block: one 1 KiB load per 16-byte column
+  static constexpr int BN = 64;          // keys per block (one PV MFMA deep)
   static constexpr int NTHR = 64 * NWM;
   static constexpr int ROWS = 32 * NWM;
   static constexpr int KC = DQK / 64;    // 64-deep d chunks of QK (one MFMA each)
@@ -148,6 +162,15 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
   float m_run = -INFINITY;
   float l_run = 0.f;
+  // Row sums of the e4m3 P (see the header): the P^T operand's lane group
+  // g = l / 16 holds the 32 P bytes of row 16 (g % 2) + l % 16 over key half
+  // g / 2.  A row 0 is e4m3 1.0 (0x38) on groups 0 and 2, A row 1 on groups 1
+  // and 3, other rows 0, so output (0, n) accumulates row n's sum and output
+  // (1, n) row n + 16's: lanes 0..15 hold them in lq[0] and lq[1].
+  const bool one_here = (lane & 15) == ((lane >> 4) & 1) && (lane & 15) < 2;
+  const uint32_t ones_w = one_here ? 0x38383838u : 0u;
+  const u32x8 ones = {ones_w, ones_w, ones_w, ones_w, ones_w, ones_w, ones_w, ones_w};
+  f32x4 lq = {0.f, 0.f, 0.f, 0.f};
 
   // LDS layout of a key block (64 rows):
   //  * K row r at r * KPITCH, chunk c at 16c (slot KSLOTS-1 is padding): the
@@ -388,6 +411,7 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     };
     if constexpr (!FIRST) {
       pv(vst, pbuf[SB ^ 1], [&](auto N_) { slot(N_); });
+      lq = mfma128_fp8(lq, ones, pbuf[SB ^ 1]);
     } else {
       static_for<NPV>([&](auto N_) { slot(N_); });
     }
@@ -401,6 +425,10 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < C::TV; ++t) acc[t] *= alpha;
+      // lq holds P up to block it - 1, like acc: lanes 0..15 scale row n's
+      // sum by their own alpha and row n + 16's by that row's
+      lq[0] *= alpha;
+      lq[1] *= __shfl(alpha, (lane & 15) + 16);
       m_run = m_new;
       const float nb2 = kPScale8Log2 - (m_run == -INFINITY ? 0.f : m_run);
       rs = 0.f;
@@ -421,17 +449,23 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
     // PV of the last block (V stage (n_iter-1) % NS == vst, P of block n_iter-1)
     __builtin_amdgcn_s_waitcnt(0);
     block_barrier();
-    if ((n_iter - 1) & 1)
+    if ((n_iter - 1) & 1) {
       pv(vst, pbuf[1], nothing);
-    else
+      lq = mfma128_fp8(lq, ones, pbuf[1]);
+    } else {
       pv(vst, pbuf[0], nothing);
+      lq = mfma128_fp8(lq, ones, pbuf[0]);
+    }
   }
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float lq_lo = __shfl(lq[0], lr & 15), lq_hi = __shfl(lq[1], lr & 15);
+  const float l_q = lr < 16 ? lq_lo : lq_hi;
   if (!row_ok) return;
   const bool live = l_tot > 0.f;
-  const float inv = live ? v_scale / l_tot : 0.f;
+  // O by the sum of the rounded weights, the LSE by the exact sum
+  const float inv = live && l_q > 0.f ? v_scale / l_q : 0.f;
   // l_run and acc both count 2^kPScale8Log2 * p: the factor cancels in O
   const float lse_v = live ? (m_run + __log2f(l_tot) - kPScale8Log2) * kLn2 : -INFINITY;
   if (S > 1) {

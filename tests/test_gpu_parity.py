@@ -144,22 +144,22 @@ def test_prefill_d256(fmha, oracle, dtype, causal):
     check(fmha, oracle, prob, splits=(1,))
 
 
-def sample_rows(prob, n_random=384, seed=0):
-    """Token/head pairs: first, last and tile-edge rows of every sequence + random."""
+def sample_rows(prob, n_random=768, seed=0):
+    """Token/head pairs: the first, last and tile-edge rows of every sequence
+    at every query head, plus random (token, head) pairs."""
     rng = np.random.default_rng(seed)
-    rows = set()
+    pairs = set()
     t0 = 0
     for sq in prob.lens_q:
-        for i in (0, 1, 15, 16, 63, 64, 127, 128, sq // 2, sq - 2, sq - 1):
+        for i in (0, 1, 15, 16, 31, 32, 63, 64, 127, 128, sq // 2, sq - 2, sq - 1):
             if 0 <= i < sq:
-                rows.add(t0 + i)
+                pairs |= {(t0 + i, h) for h in range(prob.hq)}
         t0 += sq
     tq = t0
-    rows |= set(int(x) for x in rng.integers(0, tq, size=n_random))
-    rows = sorted(rows)
-    rt = [t for t in rows for h in (0, prob.hq - 1)]
-    rh = [h for t in rows for h in (0, prob.hq - 1)]
-    return np.array(rt), np.array(rh)
+    pairs |= set(zip((int(x) for x in rng.integers(0, tq, size=n_random)),
+                     (int(x) for x in rng.integers(0, prob.hq, size=n_random))))
+    pairs = sorted(pairs)
+    return np.array([p[0] for p in pairs]), np.array([p[1] for p in pairs])
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -170,6 +170,7 @@ def test_varlen_prefill_full_sampled(fmha, oracle, lengths, causal):
     out, lse = run_gpu(fmha, prob)
     go, gl = to_packed(prob, out, lse)
     rt, rh = sample_rows(prob)
+    assert set(rh.tolist()) == set(range(prob.hq))
     ro, rl = oracle.attention_rows(raw_bits(prob.q), raw_bits(prob.k), raw_bits(prob.v),
                                    prob.dtype, rt, rh, cu_q=prob.cu_q, cu_k=prob.cu_k,
                                    scale=1 / math.sqrt(prob.dqk), causal=causal)
@@ -527,3 +528,58 @@ def test_errors_write_nothing(fmha):
                  workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert (out.float() == SENTINEL_O).all() and (lse == SENTINEL_LSE).all()
+
+
+def test_binding_rejects_mismatched_tensors(fmha):
+    # the binding checks dtype, device and shape before the library sees a
+    # pointer: an int64 cu_seqlens, an out of another dtype or shape, a short
+    # lse or a non-fp32 descale would otherwise be read or written wrongly
+    prob = fs.edge_set()
+    dev = upload(prob)
+    out, lse = alloc_outputs(prob, dev)
+    kw = dict(cu_seqlens_q=dev["cu_seqlens_q"], cu_seqlens_k=dev["cu_seqlens_k"],
+              max_seqlen_q=dev["max_seqlen_q"], max_seqlen_k=dev["max_seqlen_k"])
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    bad = [
+        dict(kw, cu_seqlens_q=dev["cu_seqlens_q"].long()),
+        dict(kw, cu_seqlens_k=dev["cu_seqlens_k"].cpu()),
+        dict(kw, out=out.float(), lse=lse),
+        dict(kw, out=out[:-1], lse=lse),
+        dict(kw, out=out, lse=lse[:, :-1]),
+        dict(kw, out=out, lse=lse.double()),
+    ]
+    for b in bad:
+        with pytest.raises(ValueError):
+            fmha.fwd(q, k, v, **b)
+    with pytest.raises(ValueError):  # a host tensor among device ones
+        fmha.fwd(q, k.cpu(), v, out=out, lse=lse, **kw)
+    f8 = fs.fp8_prefix(11008)
+    d8 = upload(f8)
+    with pytest.raises(ValueError):
+        fmha.fwd(d8["q"], d8["k"], d8["v"], q_descale=d8["q_descale"].half(),
+                 k_descale=d8["k_descale"], v_descale=d8["v_descale"])
+    torch.cuda.synchronize()
+    assert (out.float() == SENTINEL_O).all() and (lse == SENTINEL_LSE).all()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_o_unbiased(fmha, oracle, dtype):
+    # P is rounded to nearest even before the PV MFMA while the row sum adds
+    # the unrounded p, so O carries no systematic scale error: the least-squares
+    # slope of (O_gpu - O_oracle) on O_oracle stays far below one P rounding
+    # step (2^-11 relative for f16: a one-sided rounding would show a slope of
+    # about -2^-12); the max error stays within the usual tolerance
+    lens = [512] * 8
+    prob = make_problem(f"bias_{dtype}", dtype=dtype, lens_q=lens, lens_k=lens, hq=8, hkv=8,
+                        dqk=128, dv=128, seed=17, varlen_q=True, varlen_k=True)
+    ro, rl = run_oracle(oracle, prob)
+    announce(f"signed O error {dtype}")
+    out, lse = run_gpu(fmha, prob, num_kv_splits=1)
+    go, gl = to_packed(prob, out, lse)
+    compare(prob, go, gl, ro, rl, what="bias")
+    # the output rounding (to the input dtype, nearest even) is unbiased too;
+    # remove it from the comparison by rounding the oracle the same way
+    rr = torch.from_numpy(ro).to(fs.TORCH_DTYPE[dtype]).double().numpy()
+    slope = float(((go - rr) * rr).sum() / (rr * rr).sum())
+    announce(f"{dtype} prefill: O error slope {slope:.3e}")
+    assert abs(slope) < 2.0 ** -15, slope
