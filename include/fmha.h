@@ -78,7 +78,9 @@ typedef enum fmha_status {
   FMHA_OK = 0,
   FMHA_ERR_INVALID_ARG = 1, /* null/mismatched argument, Hq % Hkv != 0, bad window,
                                bad scale, bad split count, misaligned pointer/stride */
-  FMHA_ERR_UNSUPPORTED = 2, /* no compiled kernel for (dtype, head dims, out dtype) */
+  FMHA_ERR_UNSUPPORTED = 2, /* no compiled kernel for (dtype, head dims, out dtype), or
+                               token strides a kernel cannot address (prefill kernels:
+                               key block x token stride must stay below 2^31 bytes) */
   FMHA_ERR_WORKSPACE = 3,   /* split workspace missing or too small */
   FMHA_ERR_HIP = 4          /* a HIP launch or device query failed */
 } fmha_status;
@@ -202,7 +204,12 @@ typedef struct fmha_fwd_plan {
 
 /*
  * Validate `args` for an fmha_fwd call and resolve defaults, split count and
- * workspace size.  Host only: makes no HIP call and reads no device memory, so
+ * workspace size.  Defined by "Adds variable sequence lengths to the Hopper
+ * CuTe DSL FMHA example", section Implementation (the default softmax scale
+ * 1/sqrt(head_dim) for scale 0, pinned by a host test for non-square shapes;
+ * an unsupported configuration refused up front) and "[FlyDSL] Enable FP8
+ * FMHA split-K ...", review (an invalid split combination raises).
+ * Host only: makes no HIP call and reads no device memory, so
  * it runs without a GPU.  `plan` may be NULL.  The workspace pointer/size are
  * checked only when a split is used.  With args->out == NULL the arguments are
  * checked for fmha_fwd_splitkv_partials instead.  Returns FMHA_OK or an error
@@ -211,21 +218,36 @@ typedef struct fmha_fwd_plan {
 int fmha_fwd_check(const fmha_fwd_args* args, fmha_fwd_plan* plan);
 
 /* Resolved split count for `args` (host only; automatic when num_kv_splits == 0).
- * A shape query: data pointers are not checked and may be NULL. */
+ * The split choice of "[FlyDSL] Enable FP8 FMHA split-K ...", description
+ * (explicit num_kv_splits or the automatic heuristic), whose effect the split
+ * sweep of "[Cute,Fwd,Sm100] Support q_stage=1 for inference", section
+ * Benchmarks, shows.  A shape query: data pointers are not checked and may be
+ * NULL.  Returns FMHA_OK or the error code fmha_fwd_check would give. */
 int fmha_num_splits(const fmha_fwd_args* args, int32_t* splits_out);
 
-/* Workspace bytes `args` needs (host only; 0 when no split is used).  A shape
- * query: data pointers are not checked and may be NULL. */
+/* Workspace bytes `args` needs (host only; 0 when no split is used): the
+ * per-call fp32 split workspace of "[FlyDSL] Enable FP8 FMHA split-K ...",
+ * review, laid out as in fmha_fwd_plan.  A shape query: data pointers are not
+ * checked and may be NULL.  Returns FMHA_OK or an error code. */
 int fmha_fwd_workspace_size(const fmha_fwd_args* args, size_t* bytes_out);
 
 /*
  * Enqueue the forward pass on `stream`: one attention launch, plus the split
  * combine when more than one split is used.  Writes out (and lse if given).
+ * The operation of "Adds variable sequence lengths to the Hopper CuTe DSL FMHA
+ * example", sections Interface and Implementation (packed variable-length or
+ * fixed sides, rows of a query sequence without keys left unwritten), with the
+ * split-K of "[FlyDSL] Enable FP8 FMHA split-K ...", description and
+ * measurement (attention and split combine in one call, return_lse).
+ * Reads q, k, v, cu_seqlens and descales; writes only out and lse (and the
+ * workspace).  On an error nothing is enqueued (see the conventions above).
  */
 int fmha_fwd(const fmha_fwd_args* args, void* stream);
 
 /*
- * Enqueue only the attention launch of a split forward: writes the fp32
+ * Enqueue only the attention launch of a split forward (split KV as in
+ * "[Cute,Fwd,Sm100] Support q_stage=1 for inference", description: each split
+ * of the key range is its own unit of work): writes the fp32
  * partials (O_s normalised within split s, lse_s natural log; (0, -inf) for a
  * split with no allowed key) into the workspace at the plan's offsets, for
  * every split s < ceil(sk_b / chunk) of every sequence b with keys.  Requires
@@ -266,10 +288,16 @@ typedef struct fmha_combine_args {
   int32_t out_dtype;
 } fmha_combine_args;
 
-/* Enqueue the LSE-weighted combine of split partials on `stream`. */
+/* Enqueue the LSE-weighted combine of split partials on `stream`: the split
+ * combine that "[FlyDSL] Enable FP8 FMHA split-K ...", measurement and author
+ * reply, times together with the attention.  Reads o_part, lse_part and
+ * cu_seqlens; writes out and lse.  Returns FMHA_ERR_INVALID_ARG (nothing
+ * enqueued) for a bad argument, FMHA_ERR_HIP if the launch fails. */
 int fmha_splitkv_combine(const fmha_combine_args* args, void* stream);
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string; the message Python
+ * puts in its ValueError, as "[FlyDSL] Enable FP8 FMHA split-K ...", review,
+ * has invalid calls raise). */
 const char* fmha_status_str(int status);
 
 /*
@@ -290,7 +318,9 @@ const char* fmha_status_str(int status);
 int fmha_check_seqlens(const int32_t* cu_seqlens, int32_t batch, int32_t total, int32_t max_seqlen,
                        int32_t* result, void* stream);
 
-/* Compute units of the current HIP device (a HIP query; FMHA_ERR_HIP on failure). */
+/* Compute units of the current HIP device (a HIP query; FMHA_ERR_HIP on
+ * failure): the device size the automatic split choice of "[FlyDSL] Enable
+ * FP8 FMHA split-K ...", description, is sized against. */
 int fmha_device_num_cus(int32_t* num_cus_out);
 
 #ifdef __cplusplus

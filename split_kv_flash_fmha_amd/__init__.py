@@ -143,6 +143,9 @@ def check_seqlens(cu_seqlens, total: int, max_seqlen: int) -> int:
     first failing index.  Synchronises the current stream to read the result."""
     if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+    for name, val in (("total", total), ("max_seqlen", max_seqlen)):
+        if not 0 <= int(val) < 2**31:
+            raise ValueError(f"{name} must be in [0, 2**31), got {val}")
     cu = cu_seqlens.contiguous()
     res = torch.empty(1, dtype=torch.int32, device=cu.device)
     stream = torch.cuda.current_stream(cu.device).cuda_stream
@@ -166,6 +169,26 @@ def _check_tensor(name, t, ndim):
         raise ValueError(f"{name}: last dimension must be contiguous")
 
 
+def _check_device(name, t, device, dtype=None):
+    """t must live on the GPU `device` (and have `dtype` when given): the
+    library dereferences every pointer on the device."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _check_cu_seqlens(name, cu, device):
+    _check_device(name, cu, device, torch.int32)
+    if cu.dim() != 1 or cu.numel() < 1 or cu.stride(0) != 1:
+        raise ValueError(f"{name} must be a contiguous 1-D int32 tensor of batch + 1 entries")
+
+
+def _check_shape(name, t, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=None,
               max_seqlen_q=None, max_seqlen_k=None, softmax_scale=0.0, causal=False,
               window=(-1, -1), num_kv_splits=0, q_descale=None, k_descale=None,
@@ -175,10 +198,29 @@ def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=No
         raise ValueError(f"unsupported input dtype {q.dtype}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device(name, t, dev)
     vq, vk = cu_seqlens_q is not None, cu_seqlens_k is not None
     _check_tensor("q", q, 3 if vq else 4)
     _check_tensor("k", k, 3 if vk else 4)
     _check_tensor("v", v, 3 if vk else 4)
+    if vq:
+        _check_cu_seqlens("cu_seqlens_q", cu_seqlens_q, dev)
+    if vk:
+        _check_cu_seqlens("cu_seqlens_k", cu_seqlens_k, dev)
+    expect_out = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out_dtype is not None and out_dtype != expect_out:
+        raise ValueError(f"out_dtype must be {expect_out} for {q.dtype} inputs")
+    if q.dtype == torch.float8_e4m3fn:
+        for name, t in (("q_descale", q_descale), ("k_descale", k_descale),
+                        ("v_descale", v_descale)):
+            if t is not None:
+                _check_device(name, t, dev, torch.float32)
+                if t.numel() < 1:
+                    raise ValueError(f"{name} must hold one fp32 value")
+    if workspace is not None:
+        _check_device("workspace", workspace, dev)
     a = FwdArgs()
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.out, a.lse = _ptr(out), _ptr(lse)
@@ -231,14 +273,16 @@ def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=No
         a.k_stride_batch, a.k_stride_tok, a.k_stride_head = k.stride(0), k.stride(1), k.stride(2)
         a.v_stride_batch, a.v_stride_tok, a.v_stride_head = v.stride(0), v.stride(1), v.stride(2)
     if out is not None:
+        _check_device("out", out, dev, expect_out)
         _check_tensor("out", out, q.dim())
+        _check_shape("out", out, (*q.shape[:-1], dv))
         if vq:
             a.o_stride_tok, a.o_stride_head = out.stride(0), out.stride(1)
         else:
             a.o_stride_batch, a.o_stride_tok, a.o_stride_head = out.stride(0), out.stride(1), out.stride(2)
     if lse is not None:
-        if lse.dtype != torch.float32:
-            raise ValueError("lse must be float32")
+        _check_device("lse", lse, dev, torch.float32)
+        _check_shape("lse", lse, (hq, q.shape[0]) if vq else (q.shape[0], hq, q.shape[1]))
         if vq:
             a.lse_stride_head = lse.stride(0)
             if lse.stride(1) != 1:
@@ -248,9 +292,7 @@ def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=No
             if lse.stride(2) != 1:
                 raise ValueError("lse token dimension must be contiguous")
     a.in_dtype = DTYPE_CODE[q.dtype]
-    if out_dtype is None:
-        out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
-    a.out_dtype = DTYPE_CODE[out_dtype]
+    a.out_dtype = DTYPE_CODE[expect_out]
     a.q_descale, a.k_descale, a.v_descale = _ptr(q_descale), _ptr(k_descale), _ptr(v_descale)
     a.softmax_scale = float(softmax_scale or 0.0)
     a.causal = int(bool(causal))
@@ -369,15 +411,37 @@ def splitkv_combine(o_part, lse_part, *, split_chunk, out, lse=None, cu_seqlens_
     o_part [S, total_q, Hq, Dv], lse_part [S, Hq, total_q] (fp32, contiguous).
     out / lse follow the fixed-length or varlen layout of cu_seqlens_q.
     """
-    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
-        raise ValueError("partials must be float32")
-    if not o_part.is_contiguous() or not lse_part.is_contiguous():
-        raise ValueError("partials must be contiguous")
+    dev = o_part.device
+    _check_device("o_part", o_part, dev, torch.float32)
+    _check_device("lse_part", lse_part, dev, torch.float32)
+    if o_part.dim() != 4 or not o_part.is_contiguous() or not lse_part.is_contiguous():
+        raise ValueError("partials must be contiguous fp32 [S, total_q, Hq, Dv] / [S, Hq, total_q]")
     S, tq, hq, dv = o_part.shape
+    _check_shape("lse_part", lse_part, (S, hq, tq))
+    if out.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise ValueError(f"unsupported out dtype {out.dtype}")
+    _check_device("out", out, dev)
+    if out.stride(-1) != 1:
+        raise ValueError("out: last dimension must be contiguous")
+    vq = cu_seqlens_q is not None
+    if vq:
+        _check_cu_seqlens("cu_seqlens_q", cu_seqlens_q, dev)
+        _check_shape("out", out, (tq, hq, dv))
+        if lse is not None:
+            _check_device("lse", lse, dev, torch.float32)
+            _check_shape("lse", lse, (hq, tq))
+    else:
+        if out.dim() != 4 or out.shape[0] * out.shape[1] != tq:
+            raise ValueError(f"out must be [B, Sq, Hq, Dv] with B * Sq = {tq}")
+        _check_shape("out", out, (out.shape[0], out.shape[1], hq, dv))
+        if lse is not None:
+            _check_device("lse", lse, dev, torch.float32)
+            _check_shape("lse", lse, (out.shape[0], hq, out.shape[1]))
+    if cu_seqlens_k is not None:
+        _check_cu_seqlens("cu_seqlens_k", cu_seqlens_k, dev)
     a = CombineArgs()
     a.o_part, a.lse_part, a.out, a.lse = _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse)
     a.cu_seqlens_q, a.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
-    vq = cu_seqlens_q is not None
     if vq:
         a.batch = cu_seqlens_q.numel() - 1
         a.max_seqlen_q = int(max_seqlen_q)

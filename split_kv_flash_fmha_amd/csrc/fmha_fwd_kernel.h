@@ -92,13 +92,18 @@ __device__ __forceinline__ f32x4 mfma_chunk(f32x4 acc, u32x4 a, u32x4 b) {
   return acc;
 }
 
+// Two fp32 values rounded to nearest even and packed (low half = a): one
+// v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  _Float16 x = static_cast<_Float16>(a), y = static_cast<_Float16>(b);
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);

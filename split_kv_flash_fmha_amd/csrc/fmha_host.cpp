@@ -286,6 +286,12 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     if (!vk && (!stride_ok(a->k_stride_batch, eb) || !stride_ok(a->v_stride_batch, eb)))
       return FMHA_ERR_INVALID_ARG;
     if (a->lse && (a->lse_stride_head < 0 || (!vq && a->lse_stride_batch < 0))) return FMHA_ERR_INVALID_ARG;
+    // the prefill kernels address the rows of one key block with 32-bit
+    // buffer offsets (row * token stride): refuse strides that would wrap
+    if (prefill) {
+      const int64_t st = std::max(a->k_stride_tok * eb, a->v_stride_tok * eb);
+      if ((int64_t)kern->bn * st + 4096 >= ((int64_t)1 << 31)) return FMHA_ERR_UNSUPPORTED;
+    }
   }
 
   // splits
@@ -504,6 +510,7 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
   const int64_t sq_max = vq ? a->max_seqlen_q : a->seqlen_q;
   const int64_t total_q = vq ? a->total_q : (int64_t)a->batch * a->seqlen_q;
   if (sq_max < 0 || total_q < 0 || (!a->cu_seqlens_k && a->seqlen_k < 0)) return FMHA_ERR_INVALID_ARG;
+  if (total_q >= ((int64_t)1 << 31)) return FMHA_ERR_INVALID_ARG;  // partial rows are indexed in 32 bits
   if (vq && a->max_seqlen_q > a->total_q) return FMHA_ERR_INVALID_ARG;
   if (a->batch == 0 || total_q == 0 || sq_max == 0) return FMHA_OK;
   if (!a->o_part || !a->lse_part || !a->out) return FMHA_ERR_INVALID_ARG;
@@ -543,7 +550,9 @@ int fmha_splitkv_combine(const fmha_combine_args* a, void* stream) {
 
 int fmha_check_seqlens(const int32_t* cu_seqlens, int32_t batch, int32_t total, int32_t max_seqlen,
                        int32_t* result, void* stream) {
-  if (!cu_seqlens || !result || batch < 0 || total < 0 || max_seqlen < 0) return FMHA_ERR_INVALID_ARG;
+  // (the check's index loop steps by 256 and must not pass INT32_MAX)
+  if (!cu_seqlens || !result || batch < 0 || batch > INT32_MAX - 256 || total < 0 || max_seqlen < 0)
+    return FMHA_ERR_INVALID_ARG;
   if (fmha::launch_check_seqlens(cu_seqlens, batch, total, max_seqlen, result, (hipStream_t)stream) != hipSuccess)
     return FMHA_ERR_HIP;
   return FMHA_OK;

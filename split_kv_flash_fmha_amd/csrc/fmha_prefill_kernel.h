@@ -28,11 +28,12 @@
 // the other wave on the SIMD is stalled.
 //
 // Softmax bookkeeping uses a lazily moved reference max per row: p =
-// exp2(scale*s - m_ref) with m_ref moved (and O, l rescaled by
-// exp2(m_ref_old - m_ref_new)) only when some row's running max exceeds its
-// m_ref by more than kRescaleSlack (log2 units).  O and l are accumulated
-// against the same m_ref, so O = acc / l and LSE = m_ref + log2 l are exact;
-// p <= 2^kRescaleSlack keeps fp16/bf16 P in range.
+// exp2(scale*s - m_ref), with m_ref set from the first key block and moved
+// (O and l rescaled by exp2(m_ref_old - m_ref_new), the block's p recomputed)
+// only when a lane's sum of p over a block exceeds 2^12 or a row with keys in
+// the block has no reference yet.  O and l are accumulated against the same
+// m_ref, so O = acc / l and LSE = m_ref + log2 l are exact; p <= 2^12 keeps
+// fp16/bf16 P far inside their range.
 #pragma once
 #include "fmha_decode_kernel.h"
 #include "fmha_fwd_kernel.h"
@@ -60,16 +61,12 @@ __device__ __forceinline__ uint32_t pack2_in(float a, float b) {
     return pack_bf16x2(a, b);
 }
 
-constexpr float kRescaleSlack = 8.0f;
-
+// P for the PV MFMA, rounded to nearest even: the row sum adds the unrounded
+// fp32 p, so the rounding error of P averages out instead of biasing O (one
+// conversion instruction per pair for either type)
 template <int DT>
 __device__ __forceinline__ uint32_t pack2_p(float a, float b) {
-  if constexpr (DT == DT_F16) {
-    // P in [0, 2^8]: round-toward-zero packing costs one instruction per pair
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-  } else {
-    return pack_bf16x2(a, b);
-  }
+  return pack2_in<DT>(a, b);
 }
 
 template <int DT_, int D_, int NWM_, int BN_, int RT_>
@@ -540,7 +537,7 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   // Softmax with a lazily moved reference: the first block sets each row's
   // reference m_run from its max; later blocks take p = exp2(scale*s - m_run)
   // without a max and check afterwards, from the row sums, that no p exceeded
-  // 2^kSumLog2 (every p <= the sum) and that no row with keys in the block is
+  // kSumLimit (every p <= the sum) and that no row with keys in the block is
   // still without a reference.  Only then (rare) is the row max taken, O and l
   // rescaled, and the block's exponentials recomputed.  The row sum adds the
   // fp32 p (the LSE needs them unrounded).

@@ -342,3 +342,53 @@ def test_decode_split_order():
         args.update(kw)
         st, p = check(make(**args))
         assert st == OK and p.tile_order == 0, kw
+
+
+def test_prefill_token_strides_that_would_wrap_are_unsupported():
+    # the prefill kernels address the rows of one key block with 32-bit buffer
+    # offsets: a token stride whose key-block span reaches 2^31 bytes is refused
+    # up front (decode shapes use 64-bit addresses and are not limited)
+    big = (1 << 31) // (32 * 2)  # elements: 32-key block x 2-byte rows reaches 2^31 bytes
+    big -= big % 8
+    a = make(dtype=1, batch=1, sq=256, sk=256, hq=4, hkv=4, dqk=128, dv=128, splits=1)
+    st, p = check(a)
+    assert st == OK and p.kernel_id % 1000 >= 200  # a prefill kernel
+    a.k_stride_tok = big
+    assert check(a)[0] == UNSUPPORTED
+    a.k_stride_tok, a.v_stride_tok = 4 * 128, big
+    assert check(a)[0] == UNSUPPORTED
+    a.v_stride_tok = big // 2 - 4096  # half the span: fits
+    assert check(a)[0] == OK
+    d = make(dtype=2, batch=1, sq=1, sk=256, hq=4, hkv=4, dqk=128, dv=128, splits=1)
+    d.k_stride_tok = d.v_stride_tok = big
+    st, p = check(d)
+    assert st == OK and 100 <= p.kernel_id % 1000 < 200  # the decode kernel
+
+
+def test_combine_rejects_total_q_beyond_int32():
+    c = fmha.CombineArgs()
+    c.o_part = c.lse_part = c.out = FAKE
+    c.batch, c.seqlen_q, c.seqlen_k = 1 << 16, 1 << 15, 64
+    c.num_heads_q, c.head_dim_v, c.num_splits, c.split_chunk = 1, 64, 2, 32
+    c.o_stride_head, c.o_stride_tok, c.o_stride_batch = 64, 64, 64 << 15
+    c.out_dtype = 2
+    assert fmha.lib.fmha_splitkv_combine(ctypes.byref(c), None) == INVALID
+
+
+def test_check_seqlens_rejects_batch_near_int32_max():
+    f = fmha.lib.fmha_check_seqlens
+    assert f(FAKE, 2**31 - 1, 10, 10, FAKE, None) == INVALID
+    assert f(FAKE, 2**31 - 256, 10, 10, FAKE, None) == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    # every pointer the library receives is dereferenced on the GPU: the
+    # binding refuses tensors that are not on one GPU before calling it
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must be a tensor on"):
+        fmha.make_args(q, k, k)
+    cu = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fmha.check_seqlens(cu, 0, 0)
