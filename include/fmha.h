@@ -245,6 +245,23 @@ int fmha_fwd_workspace_size(const fmha_fwd_args* args, size_t* bytes_out);
 int fmha_fwd(const fmha_fwd_args* args, void* stream);
 
 /*
+ * fmha_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same launches, with the split partials in a scratch array the library holds
+ * in device memory (one per GPU it runs on, FMHA_NO_ALLOC_SCRATCH_BYTES each,
+ * kept until the process ends) instead of args->workspace, which is ignored.
+ * Makes no allocation.  The caller still passes q, k, v, out, lse.
+ * Returns FMHA_ERR_WORKSPACE (nothing enqueued) when the resolved plan needs
+ * a larger workspace than the scratch (fmha_fwd_workspace_size tells), and
+ * FMHA_ERR_HIP if the scratch address cannot be looked up; otherwise as
+ * fmha_fwd.  Every call on one GPU shares that GPU's scratch and leaves its
+ * partials there: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ */
+#define FMHA_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+int fmha_fwd_no_alloc(const fmha_fwd_args* args, void* stream);
+
+/*
  * Enqueue only the attention launch of a split forward (split KV as in
  * "[Cute,Fwd,Sm100] Support q_stage=1 for inference", description: each split
  * of the key range is its own unit of work): writes the fp32

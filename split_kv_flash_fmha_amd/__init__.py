@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = [
-    "fwd", "splitkv_partials", "splitkv_combine", "plan", "num_splits",
+    "fwd", "fwd_no_alloc", "splitkv_partials", "splitkv_combine", "plan", "num_splits",
     "workspace_size", "device_num_cus", "FwdArgs", "CombineArgs", "Plan",
     "lib", "LIB_PATH",
 ]
@@ -34,6 +34,7 @@ DTYPE_CODE = {
     torch.float8_e4m3fn: 3,
 }
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
+NO_ALLOC_SCRATCH_BYTES = 32 << 20  # FMHA_NO_ALLOC_SCRATCH_BYTES
 
 _i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                               ctypes.c_void_p, ctypes.c_size_t)
@@ -102,6 +103,7 @@ def _load():
     L.fmha_num_splits.argtypes = [P(FwdArgs), P(_i32)]
     L.fmha_fwd_workspace_size.argtypes = [P(FwdArgs), P(_sz)]
     L.fmha_fwd.argtypes = [P(FwdArgs), _vp]
+    L.fmha_fwd_no_alloc.argtypes = [P(FwdArgs), _vp]
     L.fmha_fwd_splitkv_partials.argtypes = [P(FwdArgs), _vp]
     L.fmha_splitkv_combine.argtypes = [P(CombineArgs), _vp]
     L.fmha_status_str.argtypes = [ctypes.c_int]
@@ -109,7 +111,8 @@ def _load():
     L.fmha_device_num_cus.argtypes = [P(_i32)]
     L.fmha_check_seqlens.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp]
     for f in ("fmha_fwd_check", "fmha_num_splits", "fmha_fwd_workspace_size",
-              "fmha_fwd", "fmha_fwd_splitkv_partials", "fmha_splitkv_combine",
+              "fmha_fwd", "fmha_fwd_no_alloc", "fmha_fwd_splitkv_partials",
+              "fmha_splitkv_combine",
               "fmha_device_num_cus", "fmha_check_seqlens"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -375,6 +378,26 @@ def fwd(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel() * workspace.element_size()
     _raise(lib.fmha_fwd(ctypes.byref(args), _stream()), "fmha_fwd")
+    return out, lse
+
+
+def fwd_no_alloc(q, k, v, *, out, lse=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                 max_seqlen_q=None, max_seqlen_k=None, softmax_scale=0.0, causal=False,
+                 window=(-1, -1), num_kv_splits=0, q_descale=None, k_descale=None,
+                 v_descale=None, num_cus=None):
+    """fmha_fwd_no_alloc: the forward with the split partials in the
+    library's per-GPU scratch (nothing allocated, here or in the library).
+
+    ``out`` (and ``lse`` if wanted) must be given.  Calls that overlap on one
+    GPU share the scratch and must be ordered by the caller.
+    """
+    args = make_args(q, k, v, out=out, lse=lse, cu_seqlens_q=cu_seqlens_q,
+                     cu_seqlens_k=cu_seqlens_k, max_seqlen_q=max_seqlen_q,
+                     max_seqlen_k=max_seqlen_k, softmax_scale=softmax_scale, causal=causal,
+                     window=window, num_kv_splits=num_kv_splits, q_descale=q_descale,
+                     k_descale=k_descale, v_descale=v_descale,
+                     num_cus=device_num_cus() if num_cus is None else num_cus)
+    _raise(lib.fmha_fwd_no_alloc(ctypes.byref(args), _stream()), "fmha_fwd_no_alloc")
     return out, lse
 
 

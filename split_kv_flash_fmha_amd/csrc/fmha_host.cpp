@@ -14,9 +14,16 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "../../include/fmha.h"
 #include "fmha_params.h"
+
+// Split workspace of fmha_fwd_no_alloc: one copy per GPU the library runs on,
+// held until the process ends.  In host code `scratch` is only a handle for
+// hipGetSymbolAddress; its device address (per device) is what kernels get.
+static __device__ __align__(256) char scratch[FMHA_NO_ALLOC_SCRATCH_BYTES];
 
 namespace fmha {
 namespace {
@@ -432,6 +439,50 @@ CombineParams make_combine(const fmha_fwd_args* a, const Resolved& r) {
 }  // namespace
 }  // namespace fmha
 
+namespace fmha {
+namespace {
+
+int launch_fwd(const fmha_fwd_args* args, void* stream) {
+  Resolved r;
+  int st = resolve(args, kFull, &r);
+  if (st != FMHA_OK) return st;
+  if (r.empty || r.plan.grid_main == 0) return FMHA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const FwdParams p = make_params(args, r);
+  if (r.kernel->launch(p, r.plan.grid_main, s) != hipSuccess) return FMHA_ERR_HIP;
+  if (r.plan.num_splits > 1) {
+    const CombineParams c = make_combine(args, r);
+    if (launch_combine(c, s) != hipSuccess) return FMHA_ERR_HIP;
+  }
+  return FMHA_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept for the process.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FMHA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return FMHA_ERR_HIP;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FMHA_ERR_HIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return FMHA_OK;
+}
+
+}  // namespace
+}  // namespace fmha
+
 using namespace fmha;
 
 extern "C" {
@@ -471,19 +522,19 @@ int fmha_fwd_workspace_size(const fmha_fwd_args* args, size_t* bytes_out) {
   return st;
 }
 
-int fmha_fwd(const fmha_fwd_args* args, void* stream) {
-  Resolved r;
-  int st = resolve(args, kFull, &r);
+int fmha_fwd(const fmha_fwd_args* args, void* stream) { return launch_fwd(args, stream); }
+
+int fmha_fwd_no_alloc(const fmha_fwd_args* args, void* stream) {
+  if (!args) return FMHA_ERR_INVALID_ARG;
+  fmha_fwd_args a = *args;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
   if (st != FMHA_OK) return st;
-  if (r.empty || r.plan.grid_main == 0) return FMHA_OK;
-  hipStream_t s = (hipStream_t)stream;
-  const FwdParams p = make_params(args, r);
-  if (r.kernel->launch(p, r.plan.grid_main, s) != hipSuccess) return FMHA_ERR_HIP;
-  if (r.plan.num_splits > 1) {
-    const CombineParams c = make_combine(args, r);
-    if (launch_combine(c, s) != hipSuccess) return FMHA_ERR_HIP;
-  }
-  return FMHA_OK;
+  // the split partials go to this device's scratch; resolve refuses a plan
+  // whose workspace exceeds it (FMHA_ERR_WORKSPACE) before any launch
+  a.workspace = ws;
+  a.workspace_bytes = FMHA_NO_ALLOC_SCRATCH_BYTES;
+  return launch_fwd(&a, stream);
 }
 
 int fmha_fwd_splitkv_partials(const fmha_fwd_args* args, void* stream) {
