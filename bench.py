@@ -9,10 +9,12 @@ with the headline metric (split-KV long-context decode by default: achieved
 HBM GB/s on the algorithmic bytes Q + K + V + O), a roofline object for the
 dominant kernel (its duration measured with HIP events on the launch stream)
 and the CPU oracle timed on the host as a reported baseline.  Secondary
-workloads (GQA decode, fp8 short prefix, varlen prefill) are timed by HIP
-graph replay and reported under "others"; the fp8 short prefix, whose K/V fit
-the Infinity Cache, is timed cold (replays cycle through K/V copies spanning
-1 GiB) with the warm same-buffer figure beside it.
+workloads (GQA decode, fp8 short prefix, varlen prefill) are timed as the fp8
+split-K page times its shapes (median of 7 rounds x 100 HIP graph replays of
+one forward after 5 eager and 5 graph warmups) and reported under "others";
+the fp8 short prefix, whose K/V fit the Infinity Cache, is timed cold
+(replays cycle through K/V copies spanning 1 GiB) with the warm same-buffer
+figure beside it.
 
 Algorithmic work (the accounting of the split-KV decode table on
 "[Cute,Fwd,Sm100] Support q_stage=1 for inference", section Benchmarks, pinned
@@ -284,39 +286,45 @@ def time_eager(r, steps, warmup):
     return total_ms / steps, sum(kern_ms) / len(kern_ms), wall
 
 
-def time_graph(r, calls=20, rounds=5, arg_sets=None):
-    """Median per-call time over graph replays of `calls` forwards (cycling
-    through `arg_sets` when given: cold-cache K/V)."""
+def time_graph(r, arg_sets=None, rounds=7, replays=100, eager_warmup=5, graph_warmup=5):
+    """Per-call time by HIP graph replay, as the fp8 split-K page measures:
+    5 eager and 5 graph warmups, then `rounds` rounds of `replays` replays of a
+    graph holding one forward (attention + combine), each round timed with
+    events; returns (median round mean, stdev of the round means) in ms.
+    With `arg_sets` (K/V copies: cold-cache timing) there is one graph per set
+    and the replays cycle through them."""
+    import statistics
     torch = r.torch
-    if arg_sets:
-        calls = max(calls, len(arg_sets))
-    pick = (lambda i: arg_sets[i % len(arg_sets)]) if arg_sets else (lambda i: None)
+    sets = arg_sets or [None]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(3):
-            r.step(side.cuda_stream, pick(i))
+        for i in range(eager_warmup):
+            r.step(side.cuda_stream, sets[i % len(sets)])
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            for i in range(calls):
-                r.step(side.cuda_stream, pick(i))
+    graphs = []
+    for a in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                r.step(side.cuda_stream, a)
+        graphs.append(g)
     torch.cuda.current_stream().wait_stream(side)
-    g.replay()
+    for i in range(graph_warmup):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     per = []
     for _ in range(rounds):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        g.replay()
+        for i in range(replays):
+            graphs[i % len(graphs)].replay()
         b.record()
         torch.cuda.synchronize()
-        per.append(a.elapsed_time(b) / calls)
-    per.sort()
-    return per[len(per) // 2]
+        per.append(a.elapsed_time(b) / replays)
+    return statistics.median(per), statistics.stdev(per)
 
 
 def cpu_baseline(r, sample_rows=2048):
@@ -494,16 +502,19 @@ def main():
                 continue
             o = W[name]
             ro = Runner(o, 0)
-            us = time_graph(ro) * 1e3
-            ent = dict(workload=o["desc"], us_per_call=round(us, 2),
+            med, sd = time_graph(ro)
+            us = med * 1e3
+            ent = dict(workload=o["desc"], us_per_call=round(us, 2), us_stdev=round(sd * 1e3, 2),
                        num_kv_splits=ro.plan.num_splits)
             if name.startswith("fp8"):
                 # K/V (tens of MB) fit the 256 MB Infinity Cache: the headline
                 # figure cycles through copies spanning 1 GiB (cold), the warm
                 # one replays the same buffers
                 us_warm = us
-                us = time_graph(ro, arg_sets=ro.rotated_args(1 << 30)) * 1e3
-                ent.update(us_per_call=round(us, 2), us_per_call_warm=round(us_warm, 2))
+                med, sd = time_graph(ro, arg_sets=ro.rotated_args(1 << 30))
+                us = med * 1e3
+                ent.update(us_per_call=round(us, 2), us_stdev=round(sd * 1e3, 2),
+                           us_per_call_warm=round(us_warm, 2))
             if name.startswith("varlen"):
                 tf = alg_flops(o) / (us * 1e-6) / 1e12
                 ent.update(tflops=round(tf, 1), frac_mfma_peak=round(tf / MFMA_PEAK_TFLOPS[o["dtype"]], 4))
@@ -541,6 +552,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "others": others,
+        "others_method": "per call: median of 7 rounds x 100 HIP graph replays of one forward "
+                         "(attention + combine), after 5 eager and 5 graph warmups; fp8 prefix "
+                         "cold = replays cycling through K/V copies spanning 1 GiB",
     }
     print(json.dumps(line, ensure_ascii=False))
 

@@ -199,7 +199,9 @@ typedef struct fmha_fwd_plan {
                            longest first (32-row-tile prefill kernels, one split,
                            causal or a right-only window, batch <= 64); 2: decode
                            splits, full ones first, then the partial ones longest
-                           first (decode kernel, more than one split, batch <= 64) */
+                           first (decode kernel, more than one split, batch <= 64);
+                           3: the kv heads of one (sequence, split) together
+                           (multi-row kernels, one query tile, several splits) */
 } fmha_fwd_plan;
 
 /*

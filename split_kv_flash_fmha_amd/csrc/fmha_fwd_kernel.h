@@ -197,6 +197,42 @@ __device__ __forceinline__ WorkItem grouped_item(const FwdParams& p) {
   return w;
 }
 
+// Heads-together order (kTileOrderHeadsTogether; one query tile per
+// sequence, several splits).  The splits of one kv head read disjoint key
+// ranges, so keeping them on one XCD shares nothing; the kv heads of one
+// (sequence, split) read the same tokens, whose rows are adjacent in memory
+// and share 128-byte lines when a head's row is not a multiple of 128 bytes
+// (192-byte fp8 K rows: heads 2p and 2p + 1 share one line).  Groups are
+// (sequence, split) with one item per kv head, dealt whole to XCDs in rounds
+// of 8; in the last partial round consecutive items go in pairs to one XCD
+// (blocks 8j + x and 8(j + 1) + x, j even), a remainder of fewer than 16
+// blocks block by block.
+__device__ __forceinline__ WorkItem heads_together_item(const FwdParams& p) {
+  constexpr uint32_t kXcds = 8;
+  const uint32_t bid = blockIdx.x;
+  const uint32_t gsz = (uint32_t)p.hkv;
+  const uint32_t ngroups = (uint32_t)p.batch * (uint32_t)p.num_splits;
+  const uint32_t round_items = kXcds * gsz;
+  const uint32_t full = (ngroups / kXcds) * round_items;
+  uint32_t item = bid;
+  if (bid < full) {
+    const uint32_t r = bid / round_items, local = bid % round_items;
+    item = (r * kXcds + local % kXcds) * gsz + local / kXcds;
+  } else {
+    const uint32_t k = bid - full, rest = ngroups * gsz - full;
+    if (k < rest / (2 * kXcds) * (2 * kXcds))
+      item = full + ((k / (2 * kXcds)) * kXcds + k % kXcds) * 2 + (k / kXcds) % 2;
+  }
+  WorkItem w;
+  w.qtile = 0;
+  w.hkv = (int)(item % gsz);
+  item /= gsz;
+  w.split = (int)(item % (uint32_t)p.num_splits);
+  w.b = (int)(item / (uint32_t)p.num_splits);
+  seq_span(p, w.b, w);
+  return w;
+}
+
 // Inclusive prefix sum of v over the lanes of the wave: a scan within each
 // row of 16 lanes (DPP row shifts by 1, 2, 4, 8); then row_bcast:15 adds the
 // last lane of rows 0 and 2 to rows 1 and 3, and row_bcast:31 adds lane 31
@@ -351,7 +387,7 @@ __device__ __forceinline__ bool full_first_item(const FwdParams& p, WorkItem& w)
 template <int ROWS>
 __device__ __forceinline__ bool work_item(const FwdParams& p, WorkItem& w) {
   if (p.tile_order == kTileOrderLongestFirst) return longest_first_item<ROWS>(p, w);
-  w = grouped_item(p);
+  w = p.tile_order == kTileOrderHeadsTogether ? heads_together_item(p) : grouped_item(p);
   return true;
 }
 

@@ -339,6 +339,11 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     const int64_t slots = (int64_t)a->batch * pl.num_q_tiles;
     pl.grid_main = (int64_t)a->num_heads_kv * (tiles < slots ? tiles : slots);
   }
+  // multi-row kernels with one query tile per sequence and several splits
+  // (the short cached-prefix shape): the kv heads of one split together, so
+  // neighbouring heads' rows that share 128-byte lines are fetched once per
+  // XCD
+  if (prefill && S > 1 && pl.num_q_tiles == 1 && !r->empty) pl.tile_order = kTileOrderHeadsTogether;
   // the decode kernel's splits: full ones first, then the partial ones longest
   // first (the grid keeps its (sequence, kv head, split) size; positions past
   // the last split return at once)

@@ -48,6 +48,7 @@ struct FwdParams {
 constexpr int32_t kTileOrderGrouped = 0;       // by (sequence, kv head), XCD-grouped
 constexpr int32_t kTileOrderLongestFirst = 1;  // all tiles by cost, longest first
 constexpr int32_t kTileOrderFullFirst = 2;     // decode splits: full ones, then partial ones by length
+constexpr int32_t kTileOrderHeadsTogether = 3; // one query tile, splits: the kv heads of a split on one XCD
 constexpr int kLongestFirstMaxBatch = 64;      // one sequence per lane of a wave
 
 struct CombineParams {

@@ -392,3 +392,15 @@ def test_binding_refuses_host_tensors():
     cu = torch.zeros(2, dtype=torch.int32)
     with pytest.raises(ValueError):
         fmha.check_seqlens(cu, 0, 0)
+
+
+def test_heads_together_order_for_split_short_prefix():
+    # one query tile per sequence and several splits (the fp8 short cached
+    # prefix): the kv heads of one split go together (tile order 3); with
+    # several query tiles the grouped order stays (0)
+    st, p = check(make(dtype=3, batch=1, sq=70, sk=16384, hq=12, hkv=12, dqk=192, dv=128,
+                       splits=0, workspace=FAKE, workspace_bytes=1 << 30))
+    assert st == OK and p.num_splits > 1 and p.num_q_tiles == 1 and p.tile_order == 3
+    st, p = check(make(dtype=1, batch=1, sq=600, sk=16384, hq=4, hkv=4, dqk=128, dv=128,
+                       splits=4, workspace=FAKE, workspace_bytes=1 << 30))
+    assert st == OK and p.num_q_tiles > 1 and p.tile_order == 0
