@@ -132,8 +132,21 @@ typedef enum fmha_status {
  *                 splits.
  *  workspace    : device scratch for split partials (fmha_fwd_workspace_size
  *                 bytes, 256-byte aligned); may be NULL when no split is used.
+ *                 Its counter block (fmha_fwd_plan.counter_offset, counter_bytes)
+ *                 must be zero before the first fmha_fwd that uses it; every
+ *                 call leaves it zero (allocate the workspace zeroed once and
+ *                 reuse it).  A call that finds it non-zero writes NaN rows or
+ *                 waits a bounded time, and never hangs.
  *  num_cus      : compute units used by the automatic split choice
  *                 (0 = 256, the MI355X count).
+ *  combine_mode : 0 = split partials combined by a second launch (default);
+ *                 1 = combined inside the attention launch by the split
+ *                 workgroups themselves when the plan allows it (see
+ *                 fmha_fwd_plan.combine_in_kernel), else by a second launch.
+ *                 Measured on MI355X for the fp8 short-prefix shape, the
+ *                 second launch is 6-9 % faster: both move the fp32 partials
+ *                 through memory once, and the in-kernel form adds the wait
+ *                 for a tile's slowest split.
  */
 typedef struct fmha_fwd_args {
   const void* q;
@@ -172,6 +185,7 @@ typedef struct fmha_fwd_args {
   void* workspace;
   size_t workspace_bytes;
   int32_t num_cus;
+  int32_t combine_mode;
 } fmha_fwd_args;
 
 /*
@@ -195,6 +209,16 @@ typedef struct fmha_fwd_plan {
   size_t workspace_bytes;
   size_t o_part_offset;
   size_t lse_part_offset;
+  size_t counter_offset; /* split plans: arrival counters, one 128-byte line per (sequence,
+                            kv head, query tile), counter_bytes in all */
+  size_t counter_bytes;
+  int32_t combine_in_kernel; /* 1: fmha_fwd combines the split partials inside the
+                            attention launch (no second launch): combine_mode 1,
+                            multi-row kernels whose whole grid fits one workgroup
+                            per compute unit (num_cus, checked against the device
+                            at launch), at most 64 splits.  The counter block must
+                            then be zero when the call starts; every call leaves
+                            it zero. */
   int32_t tile_order;   /* 0: tiles grouped by (sequence, kv head); 1: all tiles
                            longest first (32-row-tile prefill kernels, one split,
                            causal or a right-only window, batch <= 64); 2: decode

@@ -60,7 +60,7 @@ class FwdArgs(ctypes.Structure):
         ("window_left", _i32), ("window_right", _i32),
         ("num_kv_splits", _i32),
         ("workspace", _vp), ("workspace_bytes", _sz),
-        ("num_cus", _i32),
+        ("num_cus", _i32), ("combine_mode", _i32),
     ]
 
 
@@ -71,6 +71,7 @@ class Plan(ctypes.Structure):
         ("num_q_tiles", _i32), ("key_block", _i32), ("kernel_id", _i32),
         ("grid_main", _i64), ("grid_combine", _i64),
         ("workspace_bytes", _sz), ("o_part_offset", _sz), ("lse_part_offset", _sz),
+        ("counter_offset", _sz), ("counter_bytes", _sz), ("combine_in_kernel", _i32),
         ("tile_order", _i32),
     ]
 
@@ -195,8 +196,12 @@ def _check_shape(name, t, shape):
 def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=None,
               max_seqlen_q=None, max_seqlen_k=None, softmax_scale=0.0, causal=False,
               window=(-1, -1), num_kv_splits=0, q_descale=None, k_descale=None,
-              v_descale=None, out_dtype=None, num_cus=None, workspace=None):
-    """Fill an FwdArgs from tensors (metadata only, nothing is launched)."""
+              v_descale=None, out_dtype=None, num_cus=None, workspace=None,
+              combine_in_kernel=False):
+    """Fill an FwdArgs from tensors (metadata only, nothing is launched).
+
+    combine_in_kernel: combine split partials inside the attention launch
+    where the plan allows it (combine_mode 1) instead of a second launch."""
     if q.dtype not in DTYPE_CODE:
         raise ValueError(f"unsupported input dtype {q.dtype}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -302,6 +307,7 @@ def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=No
     a.window_left, a.window_right = int(window[0]), int(window[1])
     a.num_kv_splits = int(num_kv_splits)
     a.num_cus = int(num_cus) if num_cus is not None else 0
+    a.combine_mode = 1 if combine_in_kernel else 0
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return a
@@ -341,16 +347,18 @@ def _alloc_outputs(q, v, vq, out_dtype, return_lse):
 
 
 def _workspace(args, device):
+    """A workspace for `args`, zeroed (its arrival-counter block must start at
+    zero; every call leaves it zero, so a caller may reuse it)."""
     nbytes = workspace_size(args)
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def fwd(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
         max_seqlen_k=None, softmax_scale=0.0, causal=False, window=(-1, -1),
         num_kv_splits=0, q_descale=None, k_descale=None, v_descale=None,
-        out=None, lse=None, return_lse=True, workspace=None):
+        out=None, lse=None, return_lse=True, workspace=None, combine_in_kernel=False):
     """Attention forward.  Returns (out, lse); lse is None if return_lse=False.
 
     softmax_scale 0 means 1/sqrt(head_dim_qk); causal is bottom-right aligned;
@@ -370,7 +378,8 @@ def fwd(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
               max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
               softmax_scale=softmax_scale, causal=causal, window=window,
               num_kv_splits=num_kv_splits, q_descale=q_descale, k_descale=k_descale,
-              v_descale=v_descale, num_cus=device_num_cus())
+              v_descale=v_descale, num_cus=device_num_cus(),
+              combine_in_kernel=combine_in_kernel)
     args = make_args(q, k, v, **kw)
     if workspace is None:
         workspace = _workspace(args, q.device)

@@ -143,6 +143,12 @@ __device__ __forceinline__ u32x4 pack_p(const f32x4* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Buffer descriptor of nbytes (< 2^31) at base: raw (untyped) 32-bit offsets,
+// accesses past nbytes read zero and write nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nbytes, 0x00020000);
+}
+
 // Work item of this workgroup: (split, kv head, sequence, query tile) and the
 // sequence's query / key offsets and lengths.
 struct WorkItem {

@@ -19,6 +19,7 @@
 
 #include "../../include/fmha.h"
 #include "fmha_params.h"
+#include "fmha_fused_combine.h"
 
 // Split workspace of fmha_fwd_no_alloc: one copy per GPU the library runs on,
 // held until the process ends.  In host code `scratch` is only a handle for
@@ -226,6 +227,7 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   if (!(a->softmax_scale >= 0.f) || isinf(a->softmax_scale)) return FMHA_ERR_INVALID_ARG;
   if (a->num_kv_splits < 0 || a->num_kv_splits > FMHA_MAX_SPLITS) return FMHA_ERR_INVALID_ARG;
   if (a->num_cus < 0) return FMHA_ERR_INVALID_ARG;
+  if (a->combine_mode < 0 || a->combine_mode > 1) return FMHA_ERR_INVALID_ARG;
 
   const bool vq = a->cu_seqlens_q != nullptr, vk = a->cu_seqlens_k != nullptr;
   if (vq) {
@@ -320,7 +322,11 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     const size_t l_bytes = (size_t)S * (size_t)a->num_heads_q * (size_t)r->total_q * sizeof(float);
     pl.o_part_offset = 0;
     pl.lse_part_offset = align256(o_bytes);
-    pl.workspace_bytes = pl.lse_part_offset + align256(l_bytes);
+    // two arrival counters per (sequence, kv head, query tile) for the
+    // combine inside the attention launch
+    pl.counter_offset = pl.lse_part_offset + align256(l_bytes);
+    pl.counter_bytes = align256((size_t)a->batch * a->num_heads_kv * pl.num_q_tiles * kCounterStride * sizeof(int32_t));
+    pl.workspace_bytes = pl.counter_offset + pl.counter_bytes;
   } else {
     pl.split_chunk = (int32_t)(r->sk_max > 0 ? r->sk_max : 1);
     pl.workspace_bytes = 0;
@@ -350,7 +356,15 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   if (kern->bn == 0 && S > 1 && a->batch <= kLongestFirstMaxBatch && !r->empty)
     pl.tile_order = kTileOrderFullFirst;
   if (pl.grid_main >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
-  pl.grid_combine = (r->empty || S == 1) ? 0 : combine_grid(a->head_dim_v, S, r->sq_max * a->num_heads_q * a->batch);
+  // the split workgroups combine their partials themselves when the whole
+  // grid is resident at once (one workgroup per compute unit at most): the
+  // multi-row kernels with one round of splits, e.g. the short cached prefix
+  pl.combine_in_kernel = a->combine_mode == 1 && prefill && S > 1 && S <= kFusedMaxSplits && !r->empty &&
+                         mode != kPartials &&
+                         pl.grid_main <= num_cus && pl.lse_part_offset < ((size_t)1 << 31);
+  pl.grid_combine = (r->empty || S == 1 || pl.combine_in_kernel)
+                        ? 0
+                        : combine_grid(a->head_dim_v, S, r->sq_max * a->num_heads_q * a->batch);
   if (pl.grid_combine >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
   if (mode != kQuery && S > 1 && !r->empty) {
     if (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < pl.workspace_bytes)
@@ -371,6 +385,7 @@ FwdParams make_params(const fmha_fwd_args* a, const Resolved& r) {
   if (r.plan.num_splits > 1) {
     p.o_part = (float*)((char*)a->workspace + r.plan.o_part_offset);
     p.lse_part = (float*)((char*)a->workspace + r.plan.lse_part_offset);
+    p.counters = (int32_t*)((char*)a->workspace + r.plan.counter_offset);
   }
   p.cu_q = a->cu_seqlens_q;
   p.cu_k = a->cu_seqlens_k;
@@ -447,15 +462,31 @@ CombineParams make_combine(const fmha_fwd_args* a, const Resolved& r) {
 namespace fmha {
 namespace {
 
+// Compute units of the current device (cached per device).
+constexpr int kMaxCuDevices = 64;
+std::atomic<int> g_device_cus[kMaxCuDevices];
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxCuDevices) return 0;
+  n = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    g_device_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 int launch_fwd(const fmha_fwd_args* args, void* stream) {
   Resolved r;
   int st = resolve(args, kFull, &r);
   if (st != FMHA_OK) return st;
   if (r.empty || r.plan.grid_main == 0) return FMHA_OK;
   hipStream_t s = (hipStream_t)stream;
-  const FwdParams p = make_params(args, r);
+  FwdParams p = make_params(args, r);
+  // the in-kernel combine waits for the tile's other split workgroups: only
+  // when this device runs the whole grid at once (one workgroup per CU)
+  p.fused_combine = r.plan.combine_in_kernel && r.plan.grid_main <= device_cus();
   if (r.kernel->launch(p, r.plan.grid_main, s) != hipSuccess) return FMHA_ERR_HIP;
-  if (r.plan.num_splits > 1) {
+  if (r.plan.num_splits > 1 && !p.fused_combine) {
     const CombineParams c = make_combine(args, r);
     if (launch_combine(c, s) != hipSuccess) return FMHA_ERR_HIP;
   }

@@ -42,6 +42,8 @@ struct FwdParams {
   int32_t out_dtype;
   int32_t tile_order;    // kTileOrder*
   int32_t max_seqlen_k;  // bound on any sequence's key count
+  int32_t* counters;     // split mode: 2 per (sequence, kv head, query tile), zero between launches
+  int32_t fused_combine; // split mode: the split workgroups combine the partials themselves
 };
 
 // Block -> tile orders of the attention launch.

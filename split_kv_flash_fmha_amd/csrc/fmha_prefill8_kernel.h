@@ -32,6 +32,7 @@
 //  * Rings of LA + 2 K and V stages in LDS: the loads of LA key blocks are in
 //    flight while a block is computed.
 #pragma once
+#include "fmha_fused_combine.h"
 #include "fmha_prefill_kernel.h"
 
 namespace fmha {
@@ -462,39 +463,43 @@ __global__ __launch_bounds__(C::NTHR, 2) void fmha_prefill8_kernel(FwdParams p) 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float lq_lo = __shfl(lq[0], lr & 15), lq_hi = __shfl(lq[1], lr & 15);
   const float l_q = lr < 16 ? lq_lo : lq_hi;
-  if (!row_ok) return;
-  const bool live = l_tot > 0.f;
-  // O by the sum of the rounded weights, the LSE by the exact sum
-  const float inv = live && l_q > 0.f ? v_scale / l_q : 0.f;
-  // l_run and acc both count 2^kPScale8Log2 * p: the factor cancels in O
-  const float lse_v = live ? (m_run + __log2f(l_tot) - kPScale8Log2) * kLn2 : -INFINITY;
-  if (S > 1) {
-    const int64_t tglob = (int64_t)q_off + iq;
-    float* op = p.o_part + (((int64_t)split * p.total_q + tglob) * p.hq + hq) * C::DV;
+  if (row_ok) {
+    const bool live = l_tot > 0.f;
+    // O by the sum of the rounded weights, the LSE by the exact sum
+    const float inv = live && l_q > 0.f ? v_scale / l_q : 0.f;
+    // l_run and acc both count 2^kPScale8Log2 * p: the factor cancels in O
+    const float lse_v = live ? (m_run + __log2f(l_tot) - kPScale8Log2) * kLn2 : -INFINITY;
+    if (S > 1) {
+      const int64_t tglob = (int64_t)q_off + iq;
+      float* op = p.o_part + (((int64_t)split * p.total_q + tglob) * p.hq + hq) * C::DV;
 #pragma unroll
-    for (int t = 0; t < C::TV; ++t)
+      for (int t = 0; t < C::TV; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 o = {acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv, acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv};
-        *(f32x4*)(op + 32 * t + 8 * j + 4 * hl) = o;
+        for (int j = 0; j < 4; ++j) {
+          f32x4 o = {acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv, acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv};
+          store_partial4(op + 32 * t + 8 * j + 4 * hl, o, p.fused_combine);
+        }
+      if (hl == 0) store_partial_lse(p.lse_part + ((int64_t)split * p.hq + hq) * p.total_q + tglob, lse_v, p.fused_combine);
+    } else {
+      char* op = p.o + (p.cu_q ? (int64_t)(q_off + iq) * p.o_st : (int64_t)b * p.o_sb + (int64_t)iq * p.o_st) +
+                 (int64_t)hq * p.o_sh;
+#pragma unroll
+      for (int t = 0; t < C::TV; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x2 w = {pack_bf16x2(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
+                     pack_bf16x2(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
+          *(u32x2*)(op + (32 * t + 8 * j + 4 * hl) * 2) = w;
+        }
+      if (p.lse && hl == 0) {
+        const int64_t li = p.cu_q ? (int64_t)hq * p.lse_sh + q_off + iq : (int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + iq;
+        p.lse[li] = lse_v;
       }
-    if (hl == 0) p.lse_part[((int64_t)split * p.hq + hq) * p.total_q + tglob] = lse_v;
-  } else {
-    char* op = p.o + (p.cu_q ? (int64_t)(q_off + iq) * p.o_st : (int64_t)b * p.o_sb + (int64_t)iq * p.o_st) +
-               (int64_t)hq * p.o_sh;
-#pragma unroll
-    for (int t = 0; t < C::TV; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w = {pack_bf16x2(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
-                   pack_bf16x2(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
-        *(u32x2*)(op + (32 * t + 8 * j + 4 * hl) * 2) = w;
-      }
-    if (p.lse && hl == 0) {
-      const int64_t li = p.cu_q ? (int64_t)hq * p.lse_sh + q_off + iq : (int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + iq;
-      p.lse[li] = lse_v;
     }
   }
+  // split plans whose grid is resident at once: combine the tile's partials here
+  if (S > 1 && p.fused_combine)
+    fused_split_combine<C::NTHR, C::DV>(p, b, hkv, qtile, split, q_off, row0, min(row0 + C::ROWS, rows), sk);
 }
 
 template <class C>

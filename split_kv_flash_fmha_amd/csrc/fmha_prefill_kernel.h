@@ -36,6 +36,7 @@
 // fp16/bf16 P far inside their range.
 #pragma once
 #include "fmha_decode_kernel.h"
+#include "fmha_fused_combine.h"
 #include "fmha_fwd_kernel.h"
 
 namespace fmha {
@@ -120,9 +121,6 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, cha
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nbytes, 0x00020000);
-}
 
 // Workgroup barrier without the memory-model fences of __syncthreads(): its
 // release fence makes the compiler wait for every buffer->LDS load in flight
@@ -713,9 +711,10 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
         for (int j = 0; j < 4; ++j) {
           f32x4 o = {acc[rt][t][4 * j] * inv, acc[rt][t][4 * j + 1] * inv, acc[rt][t][4 * j + 2] * inv,
                      acc[rt][t][4 * j + 3] * inv};
-          *(f32x4*)(op + 32 * t + 8 * j + 4 * hl) = o;
+          store_partial4(op + 32 * t + 8 * j + 4 * hl, o, p.fused_combine);
         }
-      if (hl == 0) p.lse_part[((int64_t)split * p.hq + hq[rt]) * p.total_q + tglob] = lse_v;
+      if (hl == 0)
+        store_partial_lse(p.lse_part + ((int64_t)split * p.hq + hq[rt]) * p.total_q + tglob, lse_v, p.fused_combine);
     } else {
       char* op = p.o + (p.cu_q ? (int64_t)(q_off + iq[rt]) * p.o_st : (int64_t)b * p.o_sb + (int64_t)iq[rt] * p.o_st) +
                  (int64_t)hq[rt] * p.o_sh;
@@ -734,6 +733,9 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
       }
     }
   }
+  // split plans whose grid is resident at once: combine the tile's partials here
+  if (S > 1 && p.fused_combine)
+    fused_split_combine<C::NTHR, C::D>(p, b, hkv, qtile, split, q_off, row0, min(row0 + C::ROWS, rows), sk);
 }
 
 template <class C>

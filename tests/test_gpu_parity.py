@@ -7,6 +7,7 @@ every output element.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 import sys
 
@@ -229,7 +230,7 @@ def test_decode_split_order_many_sequences(fmha, oracle, batch):
                                   cu_seqlens_k=dev["cu_seqlens_k"],
                                   max_seqlen_q=dev["max_seqlen_q"],
                                   max_seqlen_k=dev["max_seqlen_k"], num_kv_splits=7,
-                                  workspace=torch.empty(16 << 20, dtype=torch.uint8,
+                                  workspace=torch.zeros(16 << 20, dtype=torch.uint8,
                                                         device="cuda")))
     assert pl.split_chunk == 96 and pl.tile_order == (2 if batch <= 64 else 0)
     check(fmha, oracle, prob, splits=(7, 0), label=f"decode order b{batch}")
@@ -463,7 +464,7 @@ def test_graph_capture_replay(fmha):
               v_descale=dev["v_descale"], out=out, lse=lse)
     ws_args = fmha.make_args(dev["q"], dev["k"], dev["v"], num_kv_splits=8,
                              num_cus=fmha.device_num_cus(), out=out, lse=lse)
-    ws = torch.empty(fmha.workspace_size(ws_args), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(fmha.workspace_size(ws_args), dtype=torch.uint8, device="cuda")
     announce("graph capture + replay")
     fmha.fwd(dev["q"], dev["k"], dev["v"], workspace=ws, **kw)
     torch.cuda.synchronize()
@@ -583,3 +584,99 @@ def test_prefill_o_unbiased(fmha, oracle, dtype):
     slope = float(((go - rr) * rr).sum() / (rr * rr).sum())
     announce(f"{dtype} prefill: O error slope {slope:.3e}")
     assert abs(slope) < 2.0 ** -15, slope
+
+
+# ---- split combine inside the attention launch ------------------------------
+
+def _f8_args(fmha, dev, out, lse, splits, ws=None):
+    a = fmha.make_args(dev["q"], dev["k"], dev["v"], out=out, lse=lse, num_kv_splits=splits,
+                       q_descale=dev["q_descale"], k_descale=dev["k_descale"],
+                       v_descale=dev["v_descale"], num_cus=fmha.device_num_cus(),
+                       combine_in_kernel=True)
+    if ws is not None:
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    return a
+
+
+def test_in_kernel_combine_matches_two_launches(fmha, oracle):
+    # fp8 short prefix (12 kv heads, one query tile): with one round of split
+    # workgroups fmha_fwd combines inside the attention launch; the result
+    # matches the partials launch + combine launch of the same plan and the
+    # oracle, and the counter block is zero again afterwards
+    prob = fs.fp8_prefix(11008)
+    ref = run_oracle(oracle, prob)
+    dev = upload(prob)
+    for splits in (0, 4, 16):
+        out, lse = alloc_outputs(prob, dev)
+        args = _f8_args(fmha, dev, out, lse, splits)
+        ws = torch.zeros(fmha.workspace_size(args), dtype=torch.uint8, device="cuda")
+        args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+        pl = fmha.plan(args)
+        assert pl.num_splits > 1 and pl.combine_in_kernel == 1 and pl.grid_combine == 0
+        announce(f"in-kernel combine, fp8 prefix 11008, {pl.num_splits} splits")
+        stream = torch.cuda.current_stream().cuda_stream
+        assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
+        torch.cuda.synchronize()
+        cb = ws[pl.counter_offset:pl.counter_offset + pl.counter_bytes]
+        assert int(cb.count_nonzero()) == 0, "counter block not left zero"
+        go, gl = to_packed(prob, out, lse)
+        compare(prob, go, gl, *ref, what=f"in-kernel combine S={pl.num_splits}")
+        # the same plan as two launches: partials, then the combine kernel
+        o2, l2 = alloc_outputs(prob, dev)
+        o_part, lse_part, pl2 = fmha.splitkv_partials(
+            dev["q"], dev["k"], dev["v"], num_kv_splits=splits, q_descale=dev["q_descale"],
+            k_descale=dev["k_descale"], v_descale=dev["v_descale"])
+        assert pl2.combine_in_kernel == 0 and pl2.split_chunk == pl.split_chunk
+        fmha.splitkv_combine(o_part, lse_part, split_chunk=pl2.split_chunk, out=o2, lse=l2,
+                             seqlen_k=prob.lens_k[0])
+        torch.cuda.synchronize()
+        g2, gl2 = to_packed(prob, o2, l2)
+        assert np.abs(go - g2).max() <= 2 ** -7 * max(1.0, np.abs(g2).max())
+        assert np.abs(gl - gl2).max() <= 1e-5
+    # graph replays: the counters return to zero after every launch, so each
+    # replay gives the eager result bit for bit
+    ref_o, ref_l = out.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(side.cuda_stream)) == 0
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep}"
+        _ = (dev["q"].float().sum() + 1).item()
+
+
+def test_in_kernel_combine_with_dirty_counters_recovers(fmha, oracle):
+    # a counter block that was not zeroed (an arrival count far past the
+    # split count) makes the tile's workgroups write NaN at once instead of
+    # waiting; the call still leaves the block zero, and the next call is right
+    prob = fs.fp8_prefix(11008)
+    dev = upload(prob)
+    out, lse = alloc_outputs(prob, dev)
+    args = _f8_args(fmha, dev, out, lse, 8)
+    ws = torch.zeros(fmha.workspace_size(args), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    pl = fmha.plan(args)
+    assert pl.combine_in_kernel == 1
+    counters = ws[pl.counter_offset:pl.counter_offset + pl.counter_bytes].view(torch.int32)
+    counters[0] = 1000  # arrival counter of (sequence 0, kv head 0, tile 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    announce("in-kernel combine with a dirty counter block")
+    assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
+    torch.cuda.synchronize()
+    assert int(counters.count_nonzero()) == 0
+    o = out.float()
+    assert torch.isnan(o[0, :, 0]).all()          # head 0 of the one sequence: NaN
+    assert not torch.isnan(o[0, :, 1:]).any()     # the other heads: combined normally
+    assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
+    torch.cuda.synchronize()
+    go, gl = to_packed(prob, out, lse)
+    compare(prob, go, gl, *run_oracle(oracle, prob), what="after a dirty counter block")

@@ -182,12 +182,16 @@ def test_explicit_splits_and_workspace_size():
     assert fmha.lib.fmha_fwd_workspace_size(ctypes.byref(a), ctypes.byref(sz)) == OK
     tq, hq, dv, S = 1, 4, 64, 4
     al = lambda x: (x + 255) // 256 * 256
-    assert sz.value == al(S * tq * hq * dv * 4) + al(S * hq * tq * 4)
+    # partials O, partials LSE, then a 128-byte line of arrival counters per
+    # (sequence, kv head, query tile), each part 256-byte aligned
+    assert sz.value == al(S * tq * hq * dv * 4) + al(S * hq * tq * 4) + al(1 * 4 * 1 * 128)
     a.workspace, a.workspace_bytes = FAKE, sz.value
     st, p = check(a)
     assert st == OK and p.num_splits == 4 and p.split_chunk * 4 >= 1024
     assert p.split_chunk % p.key_block == 0
     assert p.lse_part_offset >= S * tq * hq * dv * 4 and p.lse_part_offset % 256 == 0
+    assert p.counter_offset == p.lse_part_offset + al(S * hq * tq * 4) and p.counter_bytes == 512
+    assert p.combine_in_kernel == 0  # a decode-kernel plan: the separate combine
     a.workspace_bytes = sz.value - 1
     assert check(a)[0] == WORKSPACE
     a.workspace_bytes = sz.value
@@ -404,3 +408,32 @@ def test_heads_together_order_for_split_short_prefix():
     st, p = check(make(dtype=1, batch=1, sq=600, sk=16384, hq=4, hkv=4, dqk=128, dv=128,
                        splits=4, workspace=FAKE, workspace_bytes=1 << 30))
     assert st == OK and p.num_q_tiles > 1 and p.tile_order == 0
+
+
+def test_combine_in_kernel_only_for_resident_split_grids():
+    # fp8 short prefix: 12 kv heads x S splits on one round of workgroups ->
+    # with combine_mode 1 the combine runs inside the attention launch; not
+    # by default, not when the grid exceeds the compute units, nor for a
+    # partials-only check (out = NULL)
+    kw = dict(dtype=3, batch=1, sq=70, sk=16384, hq=12, hkv=12, dqk=192, dv=128,
+              workspace=FAKE, workspace_bytes=1 << 30)
+
+    def fused(**k):
+        a = make(**kw, **k)
+        a.combine_mode = 1
+        return a
+    st, p = check(make(splits=16, num_cus=256, **kw))
+    assert st == OK and p.combine_in_kernel == 0 and p.grid_combine > 0  # default: two launches
+    st, p = check(fused(splits=16, num_cus=256))
+    assert st == OK and p.grid_main == 192 and p.combine_in_kernel == 1 and p.grid_combine == 0
+    st, p = check(fused(splits=16, num_cus=128))
+    assert st == OK and p.combine_in_kernel == 0 and p.grid_combine > 0
+    st, p = check(fused(splits=0, num_cus=256))
+    assert st == OK and p.grid_main <= 256 and p.combine_in_kernel == 1
+    a = fused(splits=16, num_cus=256)
+    a.out = None
+    st, p = check(a)
+    assert st == OK and p.combine_in_kernel == 0
+    a = fused(splits=16, num_cus=256)
+    a.combine_mode = 2
+    assert check(a)[0] == INVALID

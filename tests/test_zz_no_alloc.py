@@ -48,7 +48,7 @@ def _no_alloc_matches(fmha, oracle, prob, splits):
     args = _args(fmha, prob, dev, out_a, lse_a, splits)
     nbytes = fmha.workspace_size(args)
     assert 0 < nbytes <= fmha.NO_ALLOC_SCRATCH_BYTES, nbytes
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     args.workspace, args.workspace_bytes = ws.data_ptr(), nbytes
     assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
     # fmha_fwd_no_alloc on the same inputs (its workspace argument is ignored)
