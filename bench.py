@@ -94,6 +94,13 @@ def workloads():
                                      fs.VARLEN_EQUAL, 16, 16, 128, 128, causal=True,
                                      varlen_q=True, varlen_k=True, seed=4,
                                      desc="varlen prefill fp16 H=16 D=128 8x2048 causal"),
+        # 128 sequences (more than the in-kernel longest-first search serves):
+        # the device-sorted tile table
+        "varlen_many_causal": _spec("varlen_many_causal", "f16", fs.many_lengths(),
+                                    fs.many_lengths(), 16, 16, 128, 128, causal=True,
+                                    varlen_q=True, varlen_k=True, seed=6,
+                                    desc="varlen prefill fp16 H=16 D=128 128 sequences "
+                                         "U[64,2048] causal"),
         # head dim 256 (the same flops per token with half the heads)
         "varlen_equal_d256": _spec("varlen_equal_d256", "f16", fs.VARLEN_EQUAL, fs.VARLEN_EQUAL,
                                    8, 8, 256, 256, varlen_q=True, varlen_k=True, seed=4,
@@ -508,7 +515,7 @@ def main():
         for name in ("gqa_decode", "fp8_prefix_16384", "fp8_prefix_16384+in_kernel_combine",
                      "fp8_prefix_11008", "varlen_skewed",
                      "varlen_skewed_causal", "varlen_equal", "varlen_equal_causal",
-                     "varlen_equal_d256", "varlen_equal_causal_d256"):
+                     "varlen_many_causal", "varlen_equal_d256", "varlen_equal_causal_d256"):
             if name == w["name"]:
                 continue
             fused = name.endswith("+in_kernel_combine")

@@ -162,6 +162,12 @@ VARLEN_EQUAL = [2048] * 8
 EDGE_LENGTHS = [1, 0, 63, 64, 65, 128, 129, 700]
 
 
+def many_lengths(seed=6, batch=128, lo=64, hi=2048):
+    """Lengths of a many-sequence varlen batch: uniform integers in [lo, hi]."""
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(lo, hi, size=batch, endpoint=True)]
+
+
 def gqa_decode_lengths(seed=2, batch=16):
     rng = np.random.default_rng(seed)
     lo, hi = GQA_DECODE_LEN_RANGE

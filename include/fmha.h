@@ -130,8 +130,10 @@ typedef enum fmha_status {
  *                 that sequence, chunk = ceil(max_seqlen_k / n) rounded up to
  *                 the kernel's key block; sequence b uses ceil(sk_b / chunk)
  *                 splits.
- *  workspace    : device scratch for split partials (fmha_fwd_workspace_size
- *                 bytes, 256-byte aligned); may be NULL when no split is used.
+ *  workspace    : device scratch for split partials and the tile table of the
+ *                 length-aware order (fmha_fwd_workspace_size bytes, 256-byte
+ *                 aligned); may be NULL when no split is used (a plan that
+ *                 would sort its tiles then keeps the grouped order).
  *                 Its counter block (fmha_fwd_plan.counter_offset, counter_bytes)
  *                 must be zero before the first fmha_fwd that uses it; every
  *                 call leaves it zero (allocate the workspace zeroed once and
@@ -219,13 +221,20 @@ typedef struct fmha_fwd_plan {
                             at launch), at most 64 splits.  The counter block must
                             then be zero when the call starts; every call leaves
                             it zero. */
+  size_t sched_offset;  /* tile_order 4: the tile table in the workspace */
+  int32_t sched_items;  /* tile_order 4: grid positions the table maps */
   int32_t tile_order;   /* 0: tiles grouped by (sequence, kv head); 1: all tiles
                            longest first (32-row-tile prefill kernels, one split,
                            causal or a right-only window, batch <= 64); 2: decode
                            splits, full ones first, then the partial ones longest
                            first (decode kernel, more than one split, batch <= 64);
                            3: the kv heads of one (sequence, split) together
-                           (multi-row kernels, one query tile, several splits) */
+                           (multi-row kernels, one query tile, several splits);
+                           4: (sequence, kv head) groups dealt to XCDs longest
+                           first by a schedule kernel on the device, each
+                           group's tiles together (32-row-tile prefill, one
+                           split, a causal or window mask, 65..1024 sequences or
+                           a left window; needs the workspace, else order 0) */
 } fmha_fwd_plan;
 
 /*

@@ -72,6 +72,7 @@ class Plan(ctypes.Structure):
         ("grid_main", _i64), ("grid_combine", _i64),
         ("workspace_bytes", _sz), ("o_part_offset", _sz), ("lse_part_offset", _sz),
         ("counter_offset", _sz), ("counter_bytes", _sz), ("combine_in_kernel", _i32),
+        ("sched_offset", _sz), ("sched_items", _i32),
         ("tile_order", _i32),
     ]
 

@@ -26,6 +26,7 @@ LIB = os.path.join(PKG, "libfmha.so")
 SOURCES = [
     "fmha_host.cpp",
     "fmha_combine.hip",
+    "fmha_schedule.hip",
     "fmha_validate.hip",
     "fmha_fwd_f32.hip",
     "fmha_fwd_f16.hip",

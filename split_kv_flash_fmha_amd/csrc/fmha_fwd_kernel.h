@@ -389,9 +389,24 @@ __device__ __forceinline__ bool full_first_item(const FwdParams& p, WorkItem& w)
   return true;
 }
 
+// Table order (kTileOrderTable): the tile the schedule kernel put at grid
+// position pos (fmha_schedule.hip), or none.
+__device__ __forceinline__ bool table_item(const FwdParams& p, int pos, WorkItem& w) {
+  const int b = p.sched[2 + 2 * pos];
+  if (b < 0) return false;
+  const int e = p.sched[3 + 2 * pos];
+  w.split = 0;
+  w.b = b;
+  w.hkv = e >> 20;
+  w.qtile = e & 0xfffff;
+  seq_span(p, b, w);
+  return true;
+}
+
 // This workgroup's item; false: nothing to do.
 template <int ROWS>
 __device__ __forceinline__ bool work_item(const FwdParams& p, WorkItem& w) {
+  if (p.tile_order == kTileOrderTable) return table_item(p, (int)blockIdx.x, w);
   if (p.tile_order == kTileOrderLongestFirst) return longest_first_item<ROWS>(p, w);
   w = p.tile_order == kTileOrderHeadsTogether ? heads_together_item(p) : grouped_item(p);
   return true;

@@ -338,12 +338,29 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   // tile that exists, a bound from the packed query count (sequence b has
   // ceil(rows_b / tile) tiles).
   pl.tile_order = kTileOrderGrouped;
-  if (prefill && S == 1 && pl.window_right >= 0 && pl.window_left < 0 &&
-      a->batch <= kLongestFirstMaxBatch && !r->empty) {
-    pl.tile_order = kTileOrderLongestFirst;
+  if (prefill && S == 1 && !r->empty && (pl.window_right >= 0 || pl.window_left >= 0)) {
     const int64_t tiles = (r->total_q * G + (int64_t)a->batch * (pl.rows_per_tile - 1)) / pl.rows_per_tile;
     const int64_t slots = (int64_t)a->batch * pl.num_q_tiles;
-    pl.grid_main = (int64_t)a->num_heads_kv * (tiles < slots ? tiles : slots);
+    const int64_t cap = tiles < slots ? tiles : slots;
+    if (pl.window_left < 0 && a->batch <= kLongestFirstMaxBatch) {
+      pl.tile_order = kTileOrderLongestFirst;
+      pl.grid_main = (int64_t)a->num_heads_kv * cap;
+    } else if (a->batch <= kScheduleMaxBatch && a->num_heads_kv < 2048 && (mode == kQuery || a->workspace)) {
+      // more sequences than lanes, or a left window: (sequence, kv head)
+      // groups dealt to XCDs longest first by a schedule kernel into a table
+      // in the workspace (without a workspace the grouped order stays).  An
+      // XCD's list holds at most a 1/8 share of the tiles plus one group
+      // (groups sorted by cost, one per XCD per round), so this many grid
+      // positions cover every tile
+      const int64_t per_xcd = ((int64_t)a->num_heads_kv * cap + 7) / 8 + pl.num_q_tiles;
+      const int64_t positions = 8 * per_xcd;
+      if (positions >= ((int64_t)1 << 29)) return FMHA_ERR_INVALID_ARG;
+      pl.tile_order = kTileOrderTable;
+      pl.grid_main = positions;
+      pl.sched_offset = 0;
+      pl.sched_items = (int32_t)positions;
+      pl.workspace_bytes = align256((size_t)(2 + 2 * positions) * sizeof(int32_t));
+    }
   }
   // multi-row kernels with one query tile per sequence and several splits
   // (the short cached-prefix shape): the kv heads of one split together, so
@@ -366,7 +383,7 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
                         ? 0
                         : combine_grid(a->head_dim_v, S, r->sq_max * a->num_heads_q * a->batch);
   if (pl.grid_combine >= kMaxGrid) return FMHA_ERR_INVALID_ARG;
-  if (mode != kQuery && S > 1 && !r->empty) {
+  if (mode != kQuery && (S > 1 || pl.tile_order == kTileOrderTable) && !r->empty) {
     if (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < pl.workspace_bytes)
       return FMHA_ERR_WORKSPACE;
   }
@@ -423,6 +440,8 @@ FwdParams make_params(const fmha_fwd_args* a, const Resolved& r) {
   p.num_q_tiles = r.plan.num_q_tiles;
   p.out_dtype = a->out_dtype;
   p.tile_order = r.plan.tile_order;
+  if (r.plan.tile_order == kTileOrderTable)
+    p.sched = (const int32_t*)((const char*)a->workspace + r.plan.sched_offset);
   p.max_seqlen_k = (int32_t)r.sk_max;
   return p;
 }
@@ -485,6 +504,10 @@ int launch_fwd(const fmha_fwd_args* args, void* stream) {
   // the in-kernel combine waits for the tile's other split workgroups: only
   // when this device runs the whole grid at once (one workgroup per CU)
   p.fused_combine = r.plan.combine_in_kernel && r.plan.grid_main <= device_cus();
+  if (r.plan.tile_order == kTileOrderTable &&
+      launch_schedule(p, r.plan.rows_per_tile, r.plan.key_block, r.plan.sched_items, (int32_t*)p.sched, s) !=
+          hipSuccess)
+    return FMHA_ERR_HIP;
   if (r.kernel->launch(p, r.plan.grid_main, s) != hipSuccess) return FMHA_ERR_HIP;
   if (r.plan.num_splits > 1 && !p.fused_combine) {
     const CombineParams c = make_combine(args, r);

@@ -43,6 +43,7 @@ struct FwdParams {
   int32_t tile_order;    // kTileOrder*
   int32_t max_seqlen_k;  // bound on any sequence's key count
   int32_t* counters;     // split mode: 2 per (sequence, kv head, query tile), zero between launches
+  const int32_t* sched;  // kTileOrderTable: the tile table written by the schedule kernel
   int32_t fused_combine; // split mode: the split workgroups combine the partials themselves
 };
 
@@ -51,6 +52,8 @@ constexpr int32_t kTileOrderGrouped = 0;       // by (sequence, kv head), XCD-gr
 constexpr int32_t kTileOrderLongestFirst = 1;  // all tiles by cost, longest first
 constexpr int32_t kTileOrderFullFirst = 2;     // decode splits: full ones, then partial ones by length
 constexpr int32_t kTileOrderHeadsTogether = 3; // one query tile, splits: the kv heads of a split on one XCD
+constexpr int32_t kTileOrderTable = 4;         // groups dealt to XCDs longest first by a schedule kernel
+constexpr int kScheduleMaxBatch = 1024;        // one sequence per thread of the schedule kernel
 constexpr int kLongestFirstMaxBatch = 64;      // one sequence per lane of a wave
 
 struct CombineParams {
@@ -119,6 +122,8 @@ inline int64_t combine_grid(int dv, int num_splits, int64_t rows) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_schedule(const FwdParams& p, int rows_per_tile, int key_block, int positions, int32_t* table,
+                           hipStream_t stream);
 hipError_t launch_check_seqlens(const int32_t* cu, int32_t batch, int32_t total, int32_t max_seqlen,
                                 int32_t* result, hipStream_t stream);
 

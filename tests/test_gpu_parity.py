@@ -188,12 +188,38 @@ def test_varlen_prefill_full_sampled(fmha, oracle, lengths, causal):
 
 # ---- tile orders: many sequences of mixed lengths --------------------------
 
-@pytest.mark.parametrize("batch", [64, 65])
-@pytest.mark.parametrize("mask", ["none", "causal", "right_window"])
+WINDOWS = {"none": (-1, -1), "causal": (-1, -1), "right_window": (-1, 40),
+           "left_window": (40, -1), "sliding": (128, 0)}
+
+
+def _tile_table_model(prob, rows_per_tile, key_block):
+    """(sequence, tile) -> cost of every existing tile (the key blocks its
+    first and last rows span, + 1), for checking the device's table."""
+    G = prob.hq // prob.hkv
+    wl, wr = prob.window
+    if prob.causal:
+        wr = 0
+    out = {}
+    for b, (sq, sk) in enumerate(zip(prob.lens_q, prob.lens_k)):
+        if sq == 0 or sk == 0:
+            continue
+        rows = sq * G
+        for t in range(-(-rows // rows_per_tile)):
+            i_lo, i_hi = t * rows_per_tile // G, (min(t * rows_per_tile + rows_per_tile, rows) - 1) // G
+            lo = max(i_lo + sk - sq - wl, 0) if wl >= 0 else 0
+            hi = min(i_hi + sk - sq + wr, sk - 1) if wr >= 0 else sk - 1
+            jb = lo // key_block * key_block
+            out[(b, t)] = (-(-(hi + 1 - jb) // key_block) if hi + 1 > jb else 0) + 1
+    return out
+
+
+@pytest.mark.parametrize("batch", [64, 65, 130, 200])
+@pytest.mark.parametrize("mask", ["none", "causal", "right_window", "left_window", "sliding"])
 def test_tile_order_many_sequences(fmha, oracle, batch, mask):
-    # causal or a right-only window: 64 sequences take the longest-first tile
-    # order, 65 the grouped one (as does no mask); the lengths mix empty
-    # sequences, q > k and k > q (rows before the first key)
+    # causal or a right-only window: up to 64 sequences take the in-kernel
+    # longest-first order, more sequences and left windows the device-sorted
+    # table; no mask the grouped order.  The lengths mix empty sequences,
+    # q > k and k > q (rows before the first key)
     rng = np.random.default_rng(batch)
     choices = [0, 1, 31, 32, 33, 95, 128, 129, 200, 257, 300]
     lens_q = [int(x) for x in rng.choice(choices, size=batch)]
@@ -202,15 +228,61 @@ def test_tile_order_many_sequences(fmha, oracle, batch, mask):
     prob = make_problem(f"tile_order_b{batch}", dtype="bf16" if mask == "none" else "f16",
                         lens_q=lens_q, lens_k=lens_k, hq=8, hkv=2, dqk=128, dv=128,
                         seed=11, varlen_q=True, varlen_k=True, causal=(mask == "causal"),
-                        window=(-1, 40) if mask == "right_window" else (-1, -1))
+                        window=WINDOWS[mask])
     dev = upload(prob)
-    pl = fmha.plan(fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
-                                  cu_seqlens_k=dev["cu_seqlens_k"],
-                                  max_seqlen_q=dev["max_seqlen_q"],
-                                  max_seqlen_k=dev["max_seqlen_k"], causal=prob.causal,
-                                  window=prob.window, num_kv_splits=1))
-    assert pl.tile_order == (1 if batch <= 64 and mask != "none" else 0)
+    args = fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                          cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+                          max_seqlen_k=dev["max_seqlen_k"], causal=prob.causal,
+                          window=prob.window, num_kv_splits=1)
+    ws = torch.zeros(max(fmha.workspace_size(args), 256), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    pl = fmha.plan(args)
+    expect = 0 if mask == "none" else (1 if batch <= 64 and mask in ("causal", "right_window")
+                                       else 4)
+    assert pl.tile_order == expect, (pl.tile_order, expect)
     check(fmha, oracle, prob, splits=(1,), label=mask)
+    if expect == 4:
+        # the table the schedule kernel wrote: every existing tile once, in
+        # non-increasing cost class
+        out, lse = alloc_outputs(prob, dev)
+        args.out, args.lse = out.data_ptr(), lse.data_ptr()
+        stream = torch.cuda.current_stream().cuda_stream
+        assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
+        torch.cuda.synchronize()
+        tab = ws[pl.sched_offset:].view(torch.int32).cpu().numpy()
+        n = int(tab[0])
+        assert n == pl.sched_items == pl.grid_main
+        model = _tile_table_model(prob, pl.rows_per_tile, pl.key_block)
+        H = prob.hkv
+        # position 8 j + x: item j of XCD x's list; lists have no holes
+        lists = [[] for _ in range(8)]
+        for pos in range(n):
+            b = int(tab[2 + 2 * pos])
+            lists[pos % 8].append(None if b < 0 else (b, int(tab[3 + 2 * pos]) >> 20,
+                                                       int(tab[3 + 2 * pos]) & 0xFFFFF))
+        got = []
+        for lst in lists:
+            k = next((i for i, e in enumerate(lst) if e is None), len(lst))
+            assert all(e is None for e in lst[k:]), "an XCD list has a hole"
+            got += lst[:k]
+            # each (sequence, kv head) group contiguous, costliest tile first
+            groups = []
+            for e in lst[:k]:
+                if not groups or groups[-1][0] != e[:2]:
+                    groups.append((e[:2], []))
+                groups[-1][1].append(model[(e[0], e[2])])
+            assert len({g[0] for g in groups}) == len(groups), "a group split within a list"
+            # (costliest first where tile costs are monotone along a sequence:
+            # every mask here but the two-sided sliding window)
+            if mask != "sliding":
+                for _, costs in groups:
+                    assert all(a >= b for a, b in zip(costs, costs[1:])), "group not costliest first"
+        want = sorted((b, h, t) for (b, t) in model for h in range(H))
+        assert sorted(got) == want, "table is not every (tile, kv head) once"
+        # groups longest first: XCD loads within two groups' cost of each other
+        load = [sum(model[(e[0], e[2])] for e in lst if e) for lst in lists]
+        gmax = max(sum(model[(b, t)] for (bb, t) in model if bb == b) for b in {b for b, _ in model})
+        assert max(load) - min(load) <= 2 * gmax
 
 
 @pytest.mark.parametrize("batch", [64, 65])

@@ -437,3 +437,42 @@ def test_combine_in_kernel_only_for_resident_split_grids():
     a = fused(splits=16, num_cus=256)
     a.combine_mode = 2
     assert check(a)[0] == INVALID
+
+
+def test_table_order_for_many_sequences_and_left_windows():
+    # masked prefill beyond the in-kernel longest-first search (more than 64
+    # sequences, or a left window) sorts its tiles on the device into a table
+    # in the workspace (tile order 4); without a workspace the grouped order
+    # stays (0)
+    al = lambda x: (x + 255) // 256 * 256
+
+    def plan(batch, causal, window, ws):
+        a = make(dtype=1, batch=batch, sq=300, sk=300, hq=8, hkv=2, dqk=128, dv=128, varlen_q=True,
+                 varlen_k=True, causal=causal, window=window, splits=1)
+        if ws:
+            a.workspace, a.workspace_bytes = FAKE, 1 << 30
+        return check(a)
+    st, p = plan(64, True, (-1, -1), True)
+    assert st == OK and p.tile_order == 1 and p.workspace_bytes == 0
+    st, p = plan(65, True, (-1, -1), True)
+    tiles = 65 * 10  # ceil(300 * 4 / 128) = 10 tiles per sequence
+    positions = 8 * ((2 * tiles + 7) // 8 + 10)  # 2 kv heads; + the longest sequence's tiles
+    assert st == OK and p.tile_order == 4 and p.sched_items == positions
+    assert p.grid_main == positions and p.workspace_bytes == al((2 + 2 * positions) * 4)
+    st, p = plan(65, True, (-1, -1), False)
+    assert st == OK and p.tile_order == 0
+    st, p = plan(8, False, (128, 0), True)
+    assert st == OK and p.tile_order == 4
+    st, p = plan(8, False, (40, -1), True)
+    assert st == OK and p.tile_order == 4
+    st, p = plan(200, False, (-1, -1), True)
+    assert st == OK and p.tile_order == 0  # no mask: grouped
+    a = make(dtype=1, batch=65, sq=300, sk=300, hq=8, hkv=2, dqk=128, dv=128, varlen_q=True,
+             varlen_k=True, causal=True, splits=1)
+    sz = ctypes.c_size_t()
+    assert fmha.lib.fmha_fwd_workspace_size(ctypes.byref(a), ctypes.byref(sz)) == OK
+    assert sz.value == al((2 + 2 * positions) * 4)
+    st, p = plan(1025, True, (-1, -1), True)
+    assert st == OK and p.tile_order == 0  # beyond the schedule kernel's sequences
+    a.workspace, a.workspace_bytes = FAKE, sz.value - 4
+    assert check(a)[0] == WORKSPACE
