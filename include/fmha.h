@@ -149,6 +149,10 @@ typedef enum fmha_status {
  *                 second launch is 6-9 % faster: both move the fp32 partials
  *                 through memory once, and the in-kernel form adds the wait
  *                 for a tile's slowest split.
+ *  persistent   : 1 = when the plan sorts its tiles on the device (tile order 4,
+ *                 f16/bf16), launch one round of workgroups that take tiles
+ *                 from the table until none is left, instead of one workgroup
+ *                 per tile; 0 = one workgroup per tile (default).
  */
 typedef struct fmha_fwd_args {
   const void* q;
@@ -188,6 +192,7 @@ typedef struct fmha_fwd_args {
   size_t workspace_bytes;
   int32_t num_cus;
   int32_t combine_mode;
+  int32_t persistent;
 } fmha_fwd_args;
 
 /*
@@ -223,6 +228,8 @@ typedef struct fmha_fwd_plan {
                             it zero. */
   size_t sched_offset;  /* tile_order 4: the tile table in the workspace */
   int32_t sched_items;  /* tile_order 4: grid positions the table maps */
+  int32_t persistent;   /* tile_order 4: 1 = a persistent grid (grid_main workgroups)
+                           takes the table's positions */
   int32_t tile_order;   /* 0: tiles grouped by (sequence, kv head); 1: all tiles
                            longest first (32-row-tile prefill kernels, one split,
                            causal or a right-only window, batch <= 64); 2: decode

@@ -60,7 +60,7 @@ class FwdArgs(ctypes.Structure):
         ("window_left", _i32), ("window_right", _i32),
         ("num_kv_splits", _i32),
         ("workspace", _vp), ("workspace_bytes", _sz),
-        ("num_cus", _i32), ("combine_mode", _i32),
+        ("num_cus", _i32), ("combine_mode", _i32), ("persistent", _i32),
     ]
 
 
@@ -72,7 +72,7 @@ class Plan(ctypes.Structure):
         ("grid_main", _i64), ("grid_combine", _i64),
         ("workspace_bytes", _sz), ("o_part_offset", _sz), ("lse_part_offset", _sz),
         ("counter_offset", _sz), ("counter_bytes", _sz), ("combine_in_kernel", _i32),
-        ("sched_offset", _sz), ("sched_items", _i32),
+        ("sched_offset", _sz), ("sched_items", _i32), ("persistent", _i32),
         ("tile_order", _i32),
     ]
 
@@ -198,11 +198,13 @@ def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=No
               max_seqlen_q=None, max_seqlen_k=None, softmax_scale=0.0, causal=False,
               window=(-1, -1), num_kv_splits=0, q_descale=None, k_descale=None,
               v_descale=None, out_dtype=None, num_cus=None, workspace=None,
-              combine_in_kernel=False):
+              combine_in_kernel=False, persistent=False):
     """Fill an FwdArgs from tensors (metadata only, nothing is launched).
 
     combine_in_kernel: combine split partials inside the attention launch
-    where the plan allows it (combine_mode 1) instead of a second launch."""
+    where the plan allows it (combine_mode 1) instead of a second launch.
+    persistent: with a device-sorted tile table (tile order 4), one round of
+    workgroups takes the tiles from it instead of one workgroup per tile."""
     if q.dtype not in DTYPE_CODE:
         raise ValueError(f"unsupported input dtype {q.dtype}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -309,6 +311,7 @@ def make_args(q, k, v, *, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=No
     a.num_kv_splits = int(num_kv_splits)
     a.num_cus = int(num_cus) if num_cus is not None else 0
     a.combine_mode = 1 if combine_in_kernel else 0
+    a.persistent = 1 if persistent else 0
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return a
@@ -359,7 +362,8 @@ def _workspace(args, device):
 def fwd(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
         max_seqlen_k=None, softmax_scale=0.0, causal=False, window=(-1, -1),
         num_kv_splits=0, q_descale=None, k_descale=None, v_descale=None,
-        out=None, lse=None, return_lse=True, workspace=None, combine_in_kernel=False):
+        out=None, lse=None, return_lse=True, workspace=None, combine_in_kernel=False,
+        persistent=False):
     """Attention forward.  Returns (out, lse); lse is None if return_lse=False.
 
     softmax_scale 0 means 1/sqrt(head_dim_qk); causal is bottom-right aligned;
@@ -380,7 +384,7 @@ def fwd(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
               softmax_scale=softmax_scale, causal=causal, window=window,
               num_kv_splits=num_kv_splits, q_descale=q_descale, k_descale=k_descale,
               v_descale=v_descale, num_cus=device_num_cus(),
-              combine_in_kernel=combine_in_kernel)
+              combine_in_kernel=combine_in_kernel, persistent=persistent)
     args = make_args(q, k, v, **kw)
     if workspace is None:
         workspace = _workspace(args, q.device)

@@ -392,9 +392,9 @@ __device__ __forceinline__ bool full_first_item(const FwdParams& p, WorkItem& w)
 // Table order (kTileOrderTable): the tile the schedule kernel put at grid
 // position pos (fmha_schedule.hip), or none.
 __device__ __forceinline__ bool table_item(const FwdParams& p, int pos, WorkItem& w) {
-  const int b = p.sched[2 + 2 * pos];
+  const int b = p.sched[kSchedHead + 2 * pos];
   if (b < 0) return false;
-  const int e = p.sched[3 + 2 * pos];
+  const int e = p.sched[kSchedHead + 1 + 2 * pos];
   w.split = 0;
   w.b = b;
   w.hkv = e >> 20;

@@ -228,6 +228,7 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
   if (a->num_kv_splits < 0 || a->num_kv_splits > FMHA_MAX_SPLITS) return FMHA_ERR_INVALID_ARG;
   if (a->num_cus < 0) return FMHA_ERR_INVALID_ARG;
   if (a->combine_mode < 0 || a->combine_mode > 1) return FMHA_ERR_INVALID_ARG;
+  if (a->persistent < 0 || a->persistent > 1) return FMHA_ERR_INVALID_ARG;
 
   const bool vq = a->cu_seqlens_q != nullptr, vk = a->cu_seqlens_k != nullptr;
   if (vq) {
@@ -357,9 +358,16 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
       if (positions >= ((int64_t)1 << 29)) return FMHA_ERR_INVALID_ARG;
       pl.tile_order = kTileOrderTable;
       pl.grid_main = positions;
+      // persistent: one round of workgroups (two per CU, one at head dim 256)
+      // takes the positions from the table (f16/bf16 prefill kernel)
+      if (a->persistent && a->in_dtype != FMHA_DTYPE_FP8_E4M3) {
+        pl.persistent = 1;
+        const int64_t round = (int64_t)num_cus * (kern->dqk >= 256 ? 1 : 2);
+        pl.grid_main = positions < round ? positions : round;
+      }
       pl.sched_offset = 0;
       pl.sched_items = (int32_t)positions;
-      pl.workspace_bytes = align256((size_t)(2 + 2 * positions) * sizeof(int32_t));
+      pl.workspace_bytes = align256((size_t)(kSchedHead + 2 * positions) * sizeof(int32_t));
     }
   }
   // multi-row kernels with one query tile per sequence and several splits
@@ -440,8 +448,10 @@ FwdParams make_params(const fmha_fwd_args* a, const Resolved& r) {
   p.num_q_tiles = r.plan.num_q_tiles;
   p.out_dtype = a->out_dtype;
   p.tile_order = r.plan.tile_order;
-  if (r.plan.tile_order == kTileOrderTable)
-    p.sched = (const int32_t*)((const char*)a->workspace + r.plan.sched_offset);
+  if (r.plan.tile_order == kTileOrderTable) {
+    p.sched = (int32_t*)((char*)a->workspace + r.plan.sched_offset);
+    p.persistent = r.plan.persistent;
+  }
   p.max_seqlen_k = (int32_t)r.sk_max;
   return p;
 }
@@ -505,7 +515,7 @@ int launch_fwd(const fmha_fwd_args* args, void* stream) {
   // when this device runs the whole grid at once (one workgroup per CU)
   p.fused_combine = r.plan.combine_in_kernel && r.plan.grid_main <= device_cus();
   if (r.plan.tile_order == kTileOrderTable &&
-      launch_schedule(p, r.plan.rows_per_tile, r.plan.key_block, r.plan.sched_items, (int32_t*)p.sched, s) !=
+      launch_schedule(p, r.plan.rows_per_tile, r.plan.key_block, r.plan.sched_items, p.sched, s) !=
           hipSuccess)
     return FMHA_ERR_HIP;
   if (r.kernel->launch(p, r.plan.grid_main, s) != hipSuccess) return FMHA_ERR_HIP;

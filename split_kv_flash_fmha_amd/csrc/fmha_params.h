@@ -43,7 +43,8 @@ struct FwdParams {
   int32_t tile_order;    // kTileOrder*
   int32_t max_seqlen_k;  // bound on any sequence's key count
   int32_t* counters;     // split mode: 2 per (sequence, kv head, query tile), zero between launches
-  const int32_t* sched;  // kTileOrderTable: the tile table written by the schedule kernel
+  int32_t* sched;        // kTileOrderTable: the tile table written by the schedule kernel
+  int32_t persistent;    // kTileOrderTable: workgroups claim table positions until none is left
   int32_t fused_combine; // split mode: the split workgroups combine the partials themselves
 };
 
@@ -54,6 +55,8 @@ constexpr int32_t kTileOrderFullFirst = 2;     // decode splits: full ones, then
 constexpr int32_t kTileOrderHeadsTogether = 3; // one query tile, splits: the kv heads of a split on one XCD
 constexpr int32_t kTileOrderTable = 4;         // groups dealt to XCDs longest first by a schedule kernel
 constexpr int kScheduleMaxBatch = 1024;        // one sequence per thread of the schedule kernel
+constexpr int kXcds = 8;                       // block i runs on XCD i % 8
+constexpr int kSchedHead = 16;                 // int32 header of the tile table
 constexpr int kLongestFirstMaxBatch = 64;      // one sequence per lane of a wave
 
 struct CombineParams {

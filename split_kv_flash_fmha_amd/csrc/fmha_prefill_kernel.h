@@ -218,12 +218,11 @@ constexpr int pvqk_need(int j) { return 3 * (j / 2) + (j % 2 ? 3 : 2); }
 // reads issued before MFMA j
 constexpr int pvqk_issued(int j, int nr) { return pvqk_need(j) + kPvqkAhead < nr ? pvqk_need(j) + kPvqkAhead : nr; }
 
+// One tile (work item wi) with the workgroup's LDS at smem.
 template <class C>
-__global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(FwdParams p) {
+__device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem& wi, char* smem) {
   constexpr int DT = C::DT;
   constexpr int RT = C::RT;
-  // 256-byte alignment: stage offsets and the XOR swizzles compose by addition
-  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -231,8 +230,6 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
   const int hl = lane >> 5;   // lane half: contraction slots / output row group
   const int lr = lane & 31;   // query row within a 32-row tile / MFMA column
 
-  WorkItem wi;
-  if (!work_item<C::ROWS>(p, wi)) return;
   const int S = p.num_splits;
   const int split = wi.split, hkv = wi.hkv, b = wi.b, qtile = wi.qtile;
   const int q_off = wi.q_off, sq = wi.sq, k_off = wi.k_off, sk = wi.sk;
@@ -738,9 +735,67 @@ __global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(Fw
     fused_split_combine<C::NTHR, C::D>(p, b, hkv, qtile, split, q_off, row0, min(row0 + C::ROWS, rows), sk);
 }
 
+// Grid position of the next tile a persistent workgroup takes: its own XCD's
+// list of the tile table first (the tiles placed there for that XCD's L2),
+// then the other lists; -1 when every list is exhausted.  The claim counters
+// only grow, so each position is taken once.  Thread 0 only.
+__device__ __forceinline__ int claim_position(const FwdParams& p, int xcc, int positions) {
+  for (int d = 0; d < kXcds; ++d) {
+    const int list = (xcc + d) % kXcds;
+    const int j = __hip_atomic_fetch_add(p.sched + 1 + list, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int pos = kXcds * j + list;
+    if (pos < positions && p.sched[kSchedHead + 2 * pos] >= 0) return pos;
+  }
+  return -1;
+}
+
+// PERSIST = false: one tile per workgroup (blockIdx.x -> work item).
+// PERSIST = true (table order): a grid of about one round of workgroups, each
+// taking table positions until none is left; the next position is claimed
+// while the current tile runs.
+template <class C, bool PERSIST>
+__global__ __launch_bounds__(C::NTHR, C::MIN_BLOCKS) void fmha_prefill_kernel(FwdParams p) {
+  // 256-byte alignment: stage offsets and the XOR swizzles compose by addition
+  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
+  if constexpr (!PERSIST) {
+    WorkItem wi;
+    if (!work_item<C::ROWS>(p, wi)) return;
+    prefill_tile<C>(p, wi, smem);
+  } else {
+    __shared__ int s_pos;
+    const int positions = p.sched[0];
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    xcc &= kXcds - 1;
+    if (threadIdx.x == 0) s_pos = claim_position(p, (int)xcc, positions);
+    __syncthreads();
+    int pos = s_pos;
+    while (pos >= 0) {
+      __syncthreads();  // every thread has read s_pos
+      // the next slot of this XCD's list, claimed now and looked at after the
+      // tile (the atomic's round trip overlaps the tile)
+      int j_next = 0;
+      if (threadIdx.x == 0)
+        j_next = __hip_atomic_fetch_add(p.sched + 1 + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      WorkItem wi;
+      if (table_item(p, pos, wi)) prefill_tile<C>(p, wi, smem);
+      if (threadIdx.x == 0) {
+        int np = kXcds * j_next + (int)xcc;
+        if (np >= positions || p.sched[kSchedHead + 2 * np] < 0) np = claim_position(p, (int)xcc, positions);
+        s_pos = np;
+      }
+      __syncthreads();  // the tile's LDS reads are done before the next tile's loads
+      pos = s_pos;
+    }
+  }
+}
+
 template <class C>
 hipError_t launch_prefill(const FwdParams& p, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL(fmha_prefill_kernel<C>, dim3((uint32_t)grid), dim3(C::NTHR), 0, stream, p);
+  if (p.persistent)
+    hipLaunchKernelGGL((fmha_prefill_kernel<C, true>), dim3((uint32_t)grid), dim3(C::NTHR), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fmha_prefill_kernel<C, false>), dim3((uint32_t)grid), dim3(C::NTHR), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -28,9 +28,9 @@
 // The grid thus covers only the tiles that exist (the plain grouped order
 // launches batch x kv heads x the longest sequence's tiles).
 //
-// Table (int32, in the workspace): [0] positions, [1] a claim counter for a
-// persistent launch (set to 0 here), [2 + 2i] sequence of position i or -1,
-// [3 + 2i] kv head << 20 | query tile.
+// Table (int32, in the workspace): [0] positions, [1 + x] how far a
+// persistent launch has claimed XCD x's list (set to 0 here), [16 + 2i]
+// sequence of position i or -1, [17 + 2i] kv head << 20 | query tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,7 +42,6 @@ namespace fmha {
 namespace {
 
 constexpr int kSchedThreads = 1024;
-constexpr int kXcds = 8;
 constexpr int kPerXcd = kSchedThreads / kXcds;  // threads scanning one XCD's list
 
 // cost of query tile t of a sequence (sq queries, sk > 0 keys)
@@ -128,8 +127,8 @@ __global__ __launch_bounds__(kSchedThreads) void fmha_schedule_kernel(FwdParams 
     for (int j = 0; j < n; ++j) {
       const int pos = kXcds * (off + j) + x;
       if (pos < positions) {
-        tab[2 + 2 * pos] = b;
-        tab[3 + 2 * pos] = (h << 20) | (s_desc[b] ? n - 1 - j : j);
+        tab[kSchedHead + 2 * pos] = b;
+        tab[kSchedHead + 1 + 2 * pos] = (h << 20) | (s_desc[b] ? n - 1 - j : j);
       }
     }
     off += n;
@@ -137,11 +136,9 @@ __global__ __launch_bounds__(kSchedThreads) void fmha_schedule_kernel(FwdParams 
   __syncthreads();
   // positions past each XCD's list hold no tile
   for (int pos = tid; pos < positions; pos += kSchedThreads)
-    if (pos / kXcds >= s_len[pos % kXcds]) tab[2 + 2 * pos] = -1;
-  if (tid == 0) {
-    tab[0] = positions;
-    tab[1] = 0;
-  }
+    if (pos / kXcds >= s_len[pos % kXcds]) tab[kSchedHead + 2 * pos] = -1;
+  if (tid == 0) tab[0] = positions;
+  if (tid < kXcds) tab[1 + tid] = 0;
 }
 
 }  // namespace

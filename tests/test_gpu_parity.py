@@ -257,9 +257,9 @@ def test_tile_order_many_sequences(fmha, oracle, batch, mask):
         # position 8 j + x: item j of XCD x's list; lists have no holes
         lists = [[] for _ in range(8)]
         for pos in range(n):
-            b = int(tab[2 + 2 * pos])
-            lists[pos % 8].append(None if b < 0 else (b, int(tab[3 + 2 * pos]) >> 20,
-                                                       int(tab[3 + 2 * pos]) & 0xFFFFF))
+            b = int(tab[16 + 2 * pos])
+            e = int(tab[17 + 2 * pos])
+            lists[pos % 8].append(None if b < 0 else (b, e >> 20, e & 0xFFFFF))
         got = []
         for lst in lists:
             k = next((i for i, e in enumerate(lst) if e is None), len(lst))
@@ -752,3 +752,35 @@ def test_in_kernel_combine_with_dirty_counters_recovers(fmha, oracle):
     torch.cuda.synchronize()
     go, gl = to_packed(prob, out, lse)
     compare(prob, go, gl, *run_oracle(oracle, prob), what="after a dirty counter block")
+
+
+@pytest.mark.parametrize("dtype,d,mask,batch", [("f16", 128, "causal", 130), ("bf16", 128, "sliding", 65),
+                                                ("f16", 256, "causal", 80), ("bf16", 64, "left_window", 20)])
+def test_persistent_table_order(fmha, oracle, dtype, d, mask, batch):
+    # a persistent grid (one round of workgroups) taking tiles from the
+    # device-sorted table, own XCD's list first: every row as the oracle
+    rng = np.random.default_rng(300 + batch)
+    choices = [0, 1, 31, 33, 95, 128, 129, 200, 257, 300, 511]
+    lens_q = [int(x) for x in rng.choice(choices, size=batch)]
+    lens_k = [int(x) for x in rng.choice(choices, size=batch)]
+    lens_q[0], lens_k[0] = 511, 511
+    prob = make_problem(f"persistent_{dtype}_{d}_{mask}", dtype=dtype, lens_q=lens_q,
+                        lens_k=lens_k, hq=8, hkv=2, dqk=d, dv=d, seed=17, varlen_q=True,
+                        varlen_k=True, causal=(mask == "causal"), window=WINDOWS[mask])
+    dev = upload(prob)
+    args = fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                          cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+                          max_seqlen_k=dev["max_seqlen_k"], causal=prob.causal,
+                          window=prob.window, num_kv_splits=1, persistent=True,
+                          num_cus=fmha.device_num_cus())
+    ws = torch.zeros(max(fmha.workspace_size(args), 256), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    pl = fmha.plan(args)
+    assert pl.tile_order == 4 and pl.persistent == 1
+    assert pl.grid_main == min(pl.sched_items, fmha.device_num_cus() * (1 if d == 256 else 2))
+    ref = run_oracle(oracle, prob)
+    for rep in range(2):
+        announce(f"persistent table order {dtype} d={d} {mask} b={batch} rep {rep}")
+        out, lse = run_gpu(fmha, prob, num_kv_splits=1, dev=dev, persistent=True)
+        go, gl = to_packed(prob, out, lse)
+        compare(prob, go, gl, *ref, what=f"persistent {mask} rep {rep}")

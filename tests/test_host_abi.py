@@ -458,7 +458,7 @@ def test_table_order_for_many_sequences_and_left_windows():
     tiles = 65 * 10  # ceil(300 * 4 / 128) = 10 tiles per sequence
     positions = 8 * ((2 * tiles + 7) // 8 + 10)  # 2 kv heads; + the longest sequence's tiles
     assert st == OK and p.tile_order == 4 and p.sched_items == positions
-    assert p.grid_main == positions and p.workspace_bytes == al((2 + 2 * positions) * 4)
+    assert p.grid_main == positions and p.workspace_bytes == al((16 + 2 * positions) * 4)
     st, p = plan(65, True, (-1, -1), False)
     assert st == OK and p.tile_order == 0
     st, p = plan(8, False, (128, 0), True)
@@ -471,8 +471,32 @@ def test_table_order_for_many_sequences_and_left_windows():
              varlen_k=True, causal=True, splits=1)
     sz = ctypes.c_size_t()
     assert fmha.lib.fmha_fwd_workspace_size(ctypes.byref(a), ctypes.byref(sz)) == OK
-    assert sz.value == al((2 + 2 * positions) * 4)
+    assert sz.value == al((16 + 2 * positions) * 4)
     st, p = plan(1025, True, (-1, -1), True)
     assert st == OK and p.tile_order == 0  # beyond the schedule kernel's sequences
     a.workspace, a.workspace_bytes = FAKE, sz.value - 4
     assert check(a)[0] == WORKSPACE
+
+
+def test_persistent_table_order_grid():
+    # persistent: one round of workgroups (two per CU; one at head dim 256)
+    # takes the table's positions; only with the table order, not for fp8
+    def plan(d, dtype=1, persistent=1, batch=130):
+        a = make(dtype=dtype, batch=batch, sq=300, sk=300, hq=8, hkv=2, dqk=d, dv=128 if dtype == 3 else d,
+                 varlen_q=True, varlen_k=True, causal=True, splits=1, num_cus=256)
+        a.workspace, a.workspace_bytes = FAKE, 1 << 30
+        a.persistent = persistent
+        return check(a)
+    st, p = plan(128)
+    assert st == OK and p.tile_order == 4 and p.persistent == 1 and p.grid_main == 512
+    st, p = plan(256)
+    assert st == OK and p.persistent == 1 and p.grid_main == 256
+    st, p = plan(128, persistent=0)
+    assert st == OK and p.persistent == 0 and p.grid_main == p.sched_items
+    st, p = plan(192, dtype=3)
+    assert st == OK and p.tile_order == 4 and p.persistent == 0
+    st, p = plan(128, batch=8)  # in-kernel longest-first order: not persistent
+    assert st == OK and p.tile_order == 1 and p.persistent == 0
+    a = make(dtype=1, batch=8, sq=300, sk=300, hq=8, hkv=2, dqk=128, dv=128, causal=True, splits=1)
+    a.persistent = 2
+    assert check(a)[0] == INVALID
