@@ -70,11 +70,15 @@ __device__ __forceinline__ uint32_t pack2_p(float a, float b) {
   return pack2_in<DT>(a, b);
 }
 
-template <int DT_, int D_, int NWM_, int BN_, int RT_>
+template <int DT_, int D_, int NWM_, int BN_, int RT_, bool PP_ = false>
 struct PfCfg {
   static constexpr int DT = DT_;
   static constexpr int D = D_;          // Dqk == Dv
   static constexpr int NWM = NWM_;      // waves
+  // two wave groups alternating MFMA and softmax phases (NWM = 8; paired
+  // timing: 3-33 % slower than two free-running 4-wave workgroups per CU, so
+  // no instance uses it)
+  static constexpr bool PP = PP_;
   static constexpr int RT = RT_;        // 32-row tiles per wave (each K/V fragment feeds RT MFMAs)
   static constexpr int BN = BN_;        // keys per block
   static constexpr int NTHR = 64 * NWM;
@@ -95,6 +99,7 @@ struct PfCfg {
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
   static_assert(1024 % ROWB == 0 && KL >= 1 && KL * NWM * 1024 == TILE, "whole 1 KiB loads per wave");
   static_assert(TILE % 256 == 0, "stage offsets keep the low address bits");
+  static_assert(!PP || (NWM % 2 == 0 && ROWB != 512), "two equal groups; loads issued in one burst");
 };
 
 // 16-byte chunk c of row r sits at chunk slot c ^ swz(r) (an XOR on the low
@@ -553,6 +558,9 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
   // slots (spread evenly)
   auto words_upto = [](int k) { return (k * RT * NWD) / (NPV + NQK); };
 
+  // two-group variant: group 1 runs one barrier behind group 0
+  const bool pp_late = C::PP && wm >= C::NWM / 2;
+
   // ST = it % 4 at compile time: every LDS stage offset is an immediate.
   // FIRST: it == 0 (no PV of a previous block; the reference is set from the
   // block max).  The last iteration also runs QK of the block after the tile
@@ -625,47 +633,82 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
       nbase[rt] = -(m_run[rt] == -INFINITY ? 0.f : m_run[rt]);
       rs[rt] = 0.f;
     }
-    // the exponentials of block it are spread over the VALU slots after the
-    // MFMAs of PV(it-1) and QK(it+1); word w of the RT * NWD words belongs to
-    // row tile w / NWD
-    auto slot = [&](auto K_) {
-      constexpr int k = decltype(K_)::value;
-      load_slot(K_);
-      static_for<words_upto(k + 1) - words_upto(k)>([&](auto W_) {
-        constexpr int w = words_upto(k) + decltype(W_)::value, rt = w / NWD;
+    // reference check (see above); has_keys: the row sees a key of this block
+    auto check_reference = [&]() {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const bool has_keys = my_lo[rt] <= j0 + C::BN - 1 && my_hi[rt] >= j0 && my_lo[rt] <= my_hi[rt];
+        if (__any(rs[rt] > kSumLimit || (m_run[rt] == -INFINITY && has_keys))) {
+          const float m_new = fmaxf(m_run[rt], row_max(rt));
+          const float alpha = fast_exp2(m_run[rt] - (m_new == -INFINITY ? 0.f : m_new));
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int t = 0; t < C::TV; ++t) acc[rt][t] *= alpha;
+          m_run[rt] = m_new;
+          const float nb2 = -(m_run[rt] == -INFINITY ? 0.f : m_run[rt]);
+          rs[rt] = 0.f;
+          static_for<NWD>([&](auto W_) { exp_word(s[rt], pc[rt], nb2, rs[rt], W_); });
+        }
+        l_run[rt] += rs[rt];
+      }
+    };
+
+    if constexpr (C::PP) {
+      // Two groups of NWM / 2 waves (rows [0, ROWS / 2) and [ROWS / 2, ROWS))
+      // run the same code with group 1 one barrier behind group 0: between two
+      // barriers one group runs the MFMA phase (PV(it-1), QK(it+1)) while the
+      // other runs the softmax phase of its previous block, so the two waves
+      // of a SIMD (one of each group) alternate between the MFMA pipe and the
+      // VALU.  Group 1 reaches the second barrier of an iteration only once
+      // its loads up to iteration it-2 have landed: group 0 passes that
+      // barrier into its next MFMA phase, which reads K(it+2) and V(it).
+      __builtin_amdgcn_s_setprio(1);
+      if constexpr (!FIRST)
+        pvqk(int_c<(ST + 3) % 4>{}, pbuf[SB ^ 1], int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], nothing);
+      else
+        qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], nothing);
+      __builtin_amdgcn_s_setprio(0);
+      if (pp_late) wait_loads(int_c<4 * C::KL>{});
+      block_barrier();
+      static_for<RT * NWD>([&](auto W_) {
+        constexpr int w = decltype(W_)::value, rt = w / NWD;
         exp_word(s[rt], pc[rt], nbase[rt], rs[rt], int_c<w % NWD>{});
       });
-    };
-    if constexpr (!FIRST) {
-      // the MFMA phase issues ahead of the other workgroup's wave on this SIMD
-      // when both are ready (paired timing: 1-1.5 % on 8x2048, causal or not)
-      __builtin_amdgcn_s_setprio(1);
-      pvqk(int_c<(ST + 3) % 4>{}, pbuf[SB ^ 1], int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(N_); });
-      __builtin_amdgcn_s_setprio(0);
+      check_reference();
     } else {
-      static_for<NPV>([&](auto N_) { slot(N_); });
-      qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(int_c<NPV + decltype(N_)::value>{}); });
-    }
-    // reference check (see above); has_keys: the row sees a key of this block
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const bool has_keys = my_lo[rt] <= j0 + C::BN - 1 && my_hi[rt] >= j0 && my_lo[rt] <= my_hi[rt];
-      if (__any(rs[rt] > kSumLimit || (m_run[rt] == -INFINITY && has_keys))) {
-        const float m_new = fmaxf(m_run[rt], row_max(rt));
-        const float alpha = fast_exp2(m_run[rt] - (m_new == -INFINITY ? 0.f : m_new));
-        l_run[rt] *= alpha;
-#pragma unroll
-        for (int t = 0; t < C::TV; ++t) acc[rt][t] *= alpha;
-        m_run[rt] = m_new;
-        const float nb2 = -(m_run[rt] == -INFINITY ? 0.f : m_run[rt]);
-        rs[rt] = 0.f;
-        static_for<NWD>([&](auto W_) { exp_word(s[rt], pc[rt], nb2, rs[rt], W_); });
+      // the exponentials of block it are spread over the VALU slots after the
+      // MFMAs of PV(it-1) and QK(it+1); word w of the RT * NWD words belongs to
+      // row tile w / NWD
+      auto slot = [&](auto K_) {
+        constexpr int k = decltype(K_)::value;
+        load_slot(K_);
+        static_for<words_upto(k + 1) - words_upto(k)>([&](auto W_) {
+          constexpr int w = words_upto(k) + decltype(W_)::value, rt = w / NWD;
+          exp_word(s[rt], pc[rt], nbase[rt], rs[rt], int_c<w % NWD>{});
+        });
+      };
+      if constexpr (!FIRST) {
+        // the MFMA phase issues ahead of the other workgroup's wave on this
+        // SIMD when both are ready (paired timing: 1-1.5 % on 8x2048, causal
+        // or not)
+        __builtin_amdgcn_s_setprio(1);
+        pvqk(int_c<(ST + 3) % 4>{}, pbuf[SB ^ 1], int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(N_); });
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        static_for<NPV>([&](auto N_) { slot(N_); });
+        qk(int_c<(ST + 1) % 4>{}, sbuf[SB ^ 1], [&](auto N_) { slot(int_c<NPV + decltype(N_)::value>{}); });
       }
-      l_run[rt] += rs[rt];
+      check_reference();
     }
   };
 
   if (n_iter > 0) {
+    // group 1 of the two-group variant: one barrier of delay (its loads up to
+    // K(1) landed first: group 0's first MFMA phase reads K(1))
+    if (pp_late) {
+      wait_loads(int_c<4 * C::KL>{});
+      block_barrier();
+    }
     body(int_c<0>{}, int_c<1>{}, 0);
     int it = 1;
     for (;;) {
@@ -689,6 +732,8 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
       case 2: pv(int_c<2>{}, pbuf[0], nothing); break;
       default: pv(int_c<3>{}, pbuf[1], nothing); break;
     }
+    // group 0 of the two-group variant matches group 1's extra barrier
+    if (C::PP && !pp_late) block_barrier();
   }
 
   // ---- epilogue, per row tile
