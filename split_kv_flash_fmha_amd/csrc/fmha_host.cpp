@@ -349,10 +349,11 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     } else if (a->batch <= kScheduleMaxBatch && a->num_heads_kv < 2048 && (mode == kQuery || a->workspace)) {
       // more sequences than lanes, or a left window: (sequence, kv head)
       // groups dealt to XCDs longest first by a schedule kernel into a table
-      // in the workspace (without a workspace the grouped order stays).  An
-      // XCD's list holds at most a 1/8 share of the tiles plus one group
-      // (groups sorted by cost, one per XCD per round), so this many grid
-      // positions cover every tile
+      // in the workspace (without a workspace the grouped order stays).  Each
+      // XCD's list gets room for a 1/8 share of the tiles plus one
+      // sequence's tiles; the schedule kernel moves what a list holds past
+      // its room to the lists with room left, and the rooms together hold
+      // every tile (kv heads x cap bounds the tiles)
       const int64_t per_xcd = ((int64_t)a->num_heads_kv * cap + 7) / 8 + pl.num_q_tiles;
       const int64_t positions = 8 * per_xcd;
       if (positions >= ((int64_t)1 << 29)) return FMHA_ERR_INVALID_ARG;

@@ -23,8 +23,13 @@
 //    holds its 1/8 share of the cost within one group's cost (each round
 //    gives it one group no larger than any of the previous round's); grid
 //    position 8 j + x holds
-//    item j of XCD x's list (the hardware sends block i to XCD i % 8), and
-//    positions past a list's end hold no tile (-1).
+//    item j of XCD x's list (the hardware sends block i to XCD i % 8);
+//  * a list has room for positions / 8 items.  Dealing by cost does not
+//    bound a list's tile count (a sequence with many query rows and few keys
+//    is cheap but has many tiles), so the items of a list past its room are
+//    moved, in order, to the free ends of the lists with room left (lowest
+//    XCD first); the host sizes the positions so that the rooms together
+//    hold every tile.  Positions past the end of a list hold no tile (-1).
 // The grid thus covers only the tiles that exist (the plain grouped order
 // launches batch x kv heads x the longest sequence's tiles).
 //
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(kSchedThreads) void fmha_schedule_kernel(FwdParams 
   __shared__ long long s_cost[kSchedThreads];
   __shared__ int s_nt[kSchedThreads], s_desc[kSchedThreads], s_order[kSchedThreads];
   __shared__ int s_part[kSchedThreads / 64];
-  __shared__ int s_len[kXcds];
+  __shared__ int s_len[kXcds], s_end[kXcds];
   const int tid = threadIdx.x;
   const int G = p.group;
   const int batch = p.batch;
@@ -120,12 +125,30 @@ __global__ __launch_bounds__(kSchedThreads) void fmha_schedule_kernel(FwdParams 
   int off = incl - mine;
   for (int w = first_wave; w < (tid >> 6); ++w) off += s_part[w];
   if (l == kPerXcd - 1) s_len[x] = off + mine;
+  __syncthreads();
+
+  // room per list; the items of a list past its room go to the free
+  // ends of the lists with room left, overflow item q to the q-th free slot
+  // counted from XCD 0 (the rooms hold every tile: positions is sized so)
+  const int room = positions / kXcds;
+  int over_before = 0;  // overflow items of the lists before this one
+  for (int y = 0; y < x; ++y) over_before += max(s_len[y] - room, 0);
+  auto place = [&](int j) {  // position of item j of this XCD's list
+    if (j < room) return kXcds * j + x;
+    int q = over_before + (j - room);
+    for (int y = 0; y < kXcds; ++y) {
+      const int free_y = max(room - s_len[y], 0);
+      if (q < free_y) return kXcds * (s_len[y] + q) + y;
+      q -= free_y;
+    }
+    return positions;  // unreachable with the host's sizing; dropped rather than written out of range
+  };
   for (int R = l * per; R < min(rounds, (l + 1) * per); ++R) {
     const int k = group_of(R);
     if (k >= ngroups) continue;
     const int b = s_order[k / H], h = k % H, n = s_nt[b];
     for (int j = 0; j < n; ++j) {
-      const int pos = kXcds * (off + j) + x;
+      const int pos = place(off + j);
       if (pos < positions) {
         tab[kSchedHead + 2 * pos] = b;
         tab[kSchedHead + 1 + 2 * pos] = (h << 20) | (s_desc[b] ? n - 1 - j : j);
@@ -134,9 +157,20 @@ __global__ __launch_bounds__(kSchedThreads) void fmha_schedule_kernel(FwdParams 
     off += n;
   }
   __syncthreads();
-  // positions past each XCD's list hold no tile
+  // positions past each list's end (its own items and the overflow placed
+  // there) hold no tile
+  if (tid == 0) {
+    int left = 0;
+    for (int y = 0; y < kXcds; ++y) left += max(s_len[y] - room, 0);
+    for (int y = 0; y < kXcds; ++y) {
+      const int free_y = max(room - s_len[y], 0), took = min(free_y, left);
+      s_end[y] = min(s_len[y], room) + took;
+      left -= took;
+    }
+  }
+  __syncthreads();
   for (int pos = tid; pos < positions; pos += kSchedThreads)
-    if (pos / kXcds >= s_len[pos % kXcds]) tab[kSchedHead + 2 * pos] = -1;
+    if (pos / kXcds >= s_end[pos % kXcds]) tab[kSchedHead + 2 * pos] = -1;
   if (tid == 0) tab[0] = positions;
   if (tid < kXcds) tab[1 + tid] = 0;
 }

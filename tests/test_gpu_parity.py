@@ -242,47 +242,88 @@ def test_tile_order_many_sequences(fmha, oracle, batch, mask):
     assert pl.tile_order == expect, (pl.tile_order, expect)
     check(fmha, oracle, prob, splits=(1,), label=mask)
     if expect == 4:
-        # the table the schedule kernel wrote: every existing tile once, in
-        # non-increasing cost class
-        out, lse = alloc_outputs(prob, dev)
-        args.out, args.lse = out.data_ptr(), lse.data_ptr()
-        stream = torch.cuda.current_stream().cuda_stream
-        assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
-        torch.cuda.synchronize()
-        tab = ws[pl.sched_offset:].view(torch.int32).cpu().numpy()
-        n = int(tab[0])
-        assert n == pl.sched_items == pl.grid_main
-        model = _tile_table_model(prob, pl.rows_per_tile, pl.key_block)
-        H = prob.hkv
-        # position 8 j + x: item j of XCD x's list; lists have no holes
-        lists = [[] for _ in range(8)]
-        for pos in range(n):
-            b = int(tab[16 + 2 * pos])
-            e = int(tab[17 + 2 * pos])
-            lists[pos % 8].append(None if b < 0 else (b, e >> 20, e & 0xFFFFF))
-        got = []
-        for lst in lists:
-            k = next((i for i, e in enumerate(lst) if e is None), len(lst))
-            assert all(e is None for e in lst[k:]), "an XCD list has a hole"
-            got += lst[:k]
-            # each (sequence, kv head) group contiguous, costliest tile first
-            groups = []
-            for e in lst[:k]:
-                if not groups or groups[-1][0] != e[:2]:
-                    groups.append((e[:2], []))
-                groups[-1][1].append(model[(e[0], e[2])])
-            assert len({g[0] for g in groups}) == len(groups), "a group split within a list"
-            # (costliest first where tile costs are monotone along a sequence:
-            # every mask here but the two-sided sliding window)
-            if mask != "sliding":
-                for _, costs in groups:
-                    assert all(a >= b for a, b in zip(costs, costs[1:])), "group not costliest first"
-        want = sorted((b, h, t) for (b, t) in model for h in range(H))
-        assert sorted(got) == want, "table is not every (tile, kv head) once"
+        _check_table(fmha, prob, dev, args, ws, pl, monotone=(mask != "sliding"), balanced=True)
+
+
+def _check_table(fmha, prob, dev, args, ws, pl, *, monotone, balanced):
+    """The table the schedule kernel wrote: every existing (tile, kv head)
+    once, lists without holes, a group's items costliest first where tile
+    costs are monotone along a sequence; optionally XCD loads balanced."""
+    out, lse = alloc_outputs(prob, dev)
+    args.out, args.lse = out.data_ptr(), lse.data_ptr()
+    stream = torch.cuda.current_stream().cuda_stream
+    assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
+    torch.cuda.synchronize()
+    tab = ws[pl.sched_offset:].view(torch.int32).cpu().numpy()
+    n = int(tab[0])
+    assert n == pl.sched_items == pl.grid_main
+    model = _tile_table_model(prob, pl.rows_per_tile, pl.key_block)
+    H = prob.hkv
+    # position 8 j + x: item j of XCD x's list; lists have no holes
+    lists = [[] for _ in range(8)]
+    for pos in range(n):
+        b = int(tab[16 + 2 * pos])
+        e = int(tab[17 + 2 * pos])
+        lists[pos % 8].append(None if b < 0 else (b, e >> 20, e & 0xFFFFF))
+    got = []
+    for lst in lists:
+        k = next((i for i, e in enumerate(lst) if e is None), len(lst))
+        assert all(e is None for e in lst[k:]), "an XCD list has a hole"
+        got += lst[:k]
+        # a group's items within one list: contiguous, costliest tile first
+        groups = []
+        for e in lst[:k]:
+            if not groups or groups[-1][0] != e[:2]:
+                groups.append((e[:2], []))
+            groups[-1][1].append(model[(e[0], e[2])])
+        assert len({g[0] for g in groups}) == len(groups), "a group split within a list"
+        if monotone:
+            for _, costs in groups:
+                assert all(a >= b for a, b in zip(costs, costs[1:])), "group not costliest first"
+    want = sorted((b, h, t) for (b, t) in model for h in range(H))
+    assert sorted(got) == want, "table is not every (tile, kv head) once"
+    if balanced:
         # groups longest first: XCD loads within two groups' cost of each other
         load = [sum(model[(e[0], e[2])] for e in lst if e) for lst in lists]
         gmax = max(sum(model[(b, t)] for (bb, t) in model if bb == b) for b in {b for b, _ in model})
         assert max(load) - min(load) <= 2 * gmax
+    return lists
+
+
+def test_tile_table_list_overflow(fmha, oracle):
+    # Dealing groups by cost does not bound an XCD list's tile count: here every
+    # sequence costs 17 key-block units (causal, GQA 4:1, 128-row tiles of 32-key
+    # blocks), but "M" sequences (512 queries, 8 keys: 15 keyless tiles + 1) have
+    # 16 tiles and "F" sequences (32 queries, 512 keys) one.  Equal costs rank by
+    # index, and the pattern M F F F F F F M puts both kv heads of every M on XCDs
+    # 0 and 1: 32 tiles per 8 sequences there against 2 elsewhere, far past a
+    # list's room (1/8 of the tile bound plus one sequence's tiles).  The
+    # schedule moves the excess to the other lists; every row must be written
+    # (the keyless ones as O = 0, LSE = -inf) and every tile listed once.
+    pattern = "MFFFFFFM" * 9
+    lens_q = [512 if c == "M" else 32 for c in pattern]
+    lens_k = [8 if c == "M" else 512 for c in pattern]
+    prob = make_problem("tile_table_overflow", dtype="f16", lens_q=lens_q, lens_k=lens_k,
+                        hq=8, hkv=2, dqk=128, dv=128, seed=14, varlen_q=True, varlen_k=True,
+                        causal=True)
+    model = _tile_table_model(prob, 128, 32)
+    costs = {b: sum(c for (bb, _), c in model.items() if bb == b) for b in range(len(pattern))}
+    assert set(costs.values()) == {17}, costs
+    dev = upload(prob)
+    args = fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                          cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+                          max_seqlen_k=dev["max_seqlen_k"], causal=True, num_kv_splits=1)
+    ws = torch.zeros(max(fmha.workspace_size(args), 256), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    pl = fmha.plan(args)
+    assert pl.tile_order == 4 and pl.rows_per_tile == 128 and pl.key_block == 32, pl
+    room = pl.sched_items // 8
+    m_tiles = 16 * pattern.count("M")  # dealt to XCD 0: one kv head of every M sequence
+    assert m_tiles > room, (m_tiles, room)
+    announce(f"tile table overflow: {len(pattern)} sequences, XCD 0 dealt {m_tiles} tiles, room {room}")
+    check(fmha, oracle, prob, splits=(1,), label="causal")
+    lists = _check_table(fmha, prob, dev, args, ws, pl, monotone=True, balanced=False)
+    assert max(sum(e is not None for e in lst) for lst in lists) <= room
 
 
 @pytest.mark.parametrize("batch", [64, 65])
