@@ -346,7 +346,8 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
     if (pl.window_left < 0 && a->batch <= kLongestFirstMaxBatch) {
       pl.tile_order = kTileOrderLongestFirst;
       pl.grid_main = (int64_t)a->num_heads_kv * cap;
-    } else if (a->batch <= kScheduleMaxBatch && a->num_heads_kv < 2048 && (mode == kQuery || a->workspace)) {
+    } else if (a->batch <= kScheduleMaxBatch && a->num_heads_kv < 2048 && pl.num_q_tiles < (1 << 20) &&
+               (int64_t)a->num_heads_kv * cap < ((int64_t)1 << 28) && (mode == kQuery || a->workspace)) {
       // more sequences than lanes, or a left window: (sequence, kv head)
       // groups dealt to XCDs longest first by a schedule kernel into a table
       // in the workspace (without a workspace the grouped order stays).  Each
@@ -355,8 +356,7 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
       // its room to the lists with room left, and the rooms together hold
       // every tile (kv heads x cap bounds the tiles)
       const int64_t per_xcd = ((int64_t)a->num_heads_kv * cap + 7) / 8 + pl.num_q_tiles;
-      const int64_t positions = 8 * per_xcd;
-      if (positions >= ((int64_t)1 << 29)) return FMHA_ERR_INVALID_ARG;
+      const int64_t positions = 8 * per_xcd;  // < 2^30 (table entries pack the tile in 20 bits)
       pl.tile_order = kTileOrderTable;
       pl.grid_main = positions;
       // persistent: one round of workgroups (two per CU, one at head dim 256)

@@ -476,6 +476,14 @@ def test_table_order_for_many_sequences_and_left_windows():
     assert st == OK and p.tile_order == 0  # beyond the schedule kernel's sequences
     a.workspace, a.workspace_bytes = FAKE, sz.value - 4
     assert check(a)[0] == WORKSPACE
+    # a table entry packs the query tile in 20 bits: a sequence of 2^20 or more
+    # 128-row tiles keeps the grouped order (a valid call, not an error)
+    for max_q, order in ((((1 << 20) - 1) * 32, 4), ((1 << 20) * 32, 0)):
+        a = make(dtype=1, batch=65, sq=300, sk=300, hq=8, hkv=2, dqk=128, dv=128, varlen_q=True,
+                 varlen_k=True, causal=True, splits=1, max_q=max_q, total_q=max_q + 64 * 300)
+        a.workspace, a.workspace_bytes = FAKE, 1 << 40
+        st, p = check(a)
+        assert st == OK and p.tile_order == order, (max_q, st, p.tile_order)
 
 
 def test_persistent_table_order_grid():
