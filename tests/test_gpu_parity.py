@@ -324,6 +324,11 @@ def test_tile_table_list_overflow(fmha, oracle):
     check(fmha, oracle, prob, splits=(1,), label="causal")
     lists = _check_table(fmha, prob, dev, args, ws, pl, monotone=True, balanced=False)
     assert max(sum(e is not None for e in lst) for lst in lists) <= room
+    # the persistent grid claims the moved items at the ends of the other lists
+    ref = run_oracle(oracle, prob)
+    out, lse = run_gpu(fmha, prob, num_kv_splits=1, dev=dev, persistent=True)
+    go, gl = to_packed(prob, out, lse)
+    compare(prob, go, gl, *ref, what="tile table overflow, persistent")
 
 
 @pytest.mark.parametrize("batch", [64, 65])
