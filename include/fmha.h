@@ -293,6 +293,9 @@ int fmha_fwd(const fmha_fwd_args* args, void* stream);
  * in device memory (one per GPU it runs on, FMHA_NO_ALLOC_SCRATCH_BYTES each,
  * kept until the process ends) instead of args->workspace, which is ignored.
  * Makes no allocation.  The caller still passes q, k, v, out, lse.
+ * combine_mode is taken as 0: the split combine always runs as the second
+ * launch (the in-launch form needs a zeroed counter block, which the shared
+ * scratch cannot promise).
  * Returns FMHA_ERR_WORKSPACE (nothing enqueued) when the resolved plan needs
  * a larger workspace than the scratch (fmha_fwd_workspace_size tells), and
  * FMHA_ERR_HIP if the scratch address cannot be looked up; otherwise as

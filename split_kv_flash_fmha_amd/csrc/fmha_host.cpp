@@ -604,6 +604,10 @@ int fmha_fwd_no_alloc(const fmha_fwd_args* args, void* stream) {
   // whose workspace exceeds it (FMHA_ERR_WORKSPACE) before any launch
   a.workspace = ws;
   a.workspace_bytes = FMHA_NO_ALLOC_SCRATCH_BYTES;
+  // the combine inside the attention launch counts arrivals in a block that
+  // must start at zero; the scratch holds whatever the previous call left, so
+  // this entry point always combines with the second launch
+  a.combine_mode = 0;
   return launch_fwd(&a, stream);
 }
 

@@ -40,7 +40,7 @@ def _args(fmha, prob, dev, out, lse, splits):
                           v_descale=dev.get("v_descale"), num_cus=fmha.device_num_cus())
 
 
-def _no_alloc_matches(fmha, oracle, prob, splits):
+def _no_alloc_matches(fmha, oracle, prob, splits, combine_mode_b=0):
     dev = upload(prob)
     stream = torch.cuda.current_stream().cuda_stream
     # fmha_fwd with the caller's workspace
@@ -55,6 +55,7 @@ def _no_alloc_matches(fmha, oracle, prob, splits):
     out_b, lse_b = alloc_outputs(prob, dev)
     args_b = _args(fmha, prob, dev, out_b, lse_b, splits)
     args_b.workspace, args_b.workspace_bytes = None, 0
+    args_b.combine_mode = combine_mode_b
     assert fmha.lib.fmha_fwd_no_alloc(ctypes.byref(args_b), ctypes.c_void_p(stream)) == 0
     torch.cuda.synchronize()
     # same kernels, same plan: identical bits; and the oracle's tolerance
@@ -85,6 +86,21 @@ def test_no_alloc_fp8_short_prefix(fmha, oracle):
     prob = fs.fp8_prefix(11008)
     announce("no_alloc: fp8 short prefix, auto splits")
     _no_alloc_matches(fmha, oracle, prob, 0)
+
+
+def test_no_alloc_ignores_the_in_launch_combine(fmha, oracle):
+    # the fp8 prefix is a plan the in-launch combine serves (combine_mode 1 with
+    # a zeroed workspace); on the scratch, which the GQA decode call before it
+    # leaves full of partials, no_alloc must take the two-launch path: the bits
+    # of fmha_fwd's default call, not NaN rows from a dirty counter block
+    lens_k = [30000, 1200, 17777, 4096, 25000, 9000, 1, 31000]
+    big = make_problem("no_alloc_dirty", dtype="bf16", lens_q=[1] * 8, lens_k=lens_k, hq=32,
+                       hkv=8, dqk=128, dv=128, seed=44, varlen_q=False, varlen_k=True)
+    announce("no_alloc: GQA decode leaves the scratch dirty")
+    _no_alloc_matches(fmha, oracle, big, 0)
+    prob = fs.fp8_prefix(11008)
+    announce("no_alloc: fp8 short prefix asking for the in-launch combine")
+    _no_alloc_matches(fmha, oracle, prob, 0, combine_mode_b=1)
 
 
 def test_no_alloc_refuses_plans_beyond_the_scratch(fmha):
