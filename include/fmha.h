@@ -148,7 +148,12 @@ typedef enum fmha_status {
  *                 Measured on MI355X for the fp8 short-prefix shape, the
  *                 second launch is 6-9 % faster: both move the fp32 partials
  *                 through memory once, and the in-kernel form adds the wait
- *                 for a tile's slowest split.
+ *                 for a tile's slowest split.  The plan takes this form only
+ *                 when its grid fits the device's compute units, assuming the
+ *                 launch has them to itself: a split workgroup kept from
+ *                 starting for longer than the bounded wait (about a quarter
+ *                 of a second; e.g. behind a long kernel on another stream)
+ *                 makes its tile's rows NaN instead of hanging.
  *  persistent   : 1 = when the plan sorts its tiles on the device (tile order 4,
  *                 f16/bf16), launch one round of workgroups that take tiles
  *                 from the table until none is left, instead of one workgroup
