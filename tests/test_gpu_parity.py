@@ -331,6 +331,44 @@ def test_tile_table_list_overflow(fmha, oracle):
     compare(prob, go, gl, *ref, what="tile table overflow, persistent")
 
 
+def test_tile_table_random_mixes(fmha):
+    # the device schedule on many seeded length mixes (tables only, no oracle):
+    # sequences with many queries and few keys (cheap but many tiles), the
+    # reverse, empty ones and long ones, 65..300 sequences, three masks, GQA
+    # 4:1 and 1:1, head dims 64 and 128; every table must list every (tile, kv
+    # head) once, without holes, each group costliest first where costs are
+    # monotone
+    menu = [(0, 7), (5, 0), (1, 900), (32, 512), (512, 8), (300, 300), (129, 2000), (2000, 40),
+            (64, 64), (700, 1)]
+    cases = 0
+    for seed in range(24):
+        rng = np.random.default_rng(1000 + seed)
+        batch = int(rng.integers(65, 301))
+        picks = rng.integers(0, len(menu), batch)
+        lens_q = [menu[i][0] for i in picks]
+        lens_k = [menu[i][1] for i in picks]
+        lens_q[0], lens_k[0] = 300, 300
+        mask = ("causal", "left_window", "sliding")[seed % 3]
+        hq, hkv = ((8, 2), (4, 4))[seed % 2]
+        d = (64, 128)[(seed // 2) % 2]  # 64- and 32-key blocks
+        prob = make_problem(f"tile_mix_{seed}", dtype="f16", lens_q=lens_q, lens_k=lens_k, hq=hq,
+                            hkv=hkv, dqk=d, dv=d, seed=seed, varlen_q=True, varlen_k=True,
+                            causal=(mask == "causal"), window=WINDOWS[mask])
+        dev = upload(prob)
+        args = fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                              cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+                              max_seqlen_k=dev["max_seqlen_k"], causal=prob.causal,
+                              window=prob.window, num_kv_splits=1)
+        ws = torch.zeros(max(fmha.workspace_size(args), 256), dtype=torch.uint8, device="cuda")
+        args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+        pl = fmha.plan(args)
+        assert pl.tile_order == 4, (seed, pl.tile_order)
+        announce(f"tile table mix {seed}: {batch} sequences, {mask}, GQA {hq}:{hkv}")
+        _check_table(fmha, prob, dev, args, ws, pl, monotone=(mask != "sliding"), balanced=False)
+        cases += 1
+    assert cases == 24
+
+
 @pytest.mark.parametrize("batch", [64, 65])
 def test_decode_split_order_many_sequences(fmha, oracle, batch):
     # decode with splits: 64 sequences take the full-first split order, 65 the
