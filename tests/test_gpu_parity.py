@@ -331,6 +331,33 @@ def test_tile_table_list_overflow(fmha, oracle):
     compare(prob, go, gl, *ref, what="tile table overflow, persistent")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_longest_first_random_mixes(fmha, oracle, seed):
+    # the in-kernel longest-first order (up to 64 sequences, causal or a right
+    # window) on seeded length mixes with keyless tiles (many queries, few
+    # keys), keyless sequences and long ones: every row as the oracle
+    menu = [(0, 7), (5, 0), (1, 900), (32, 512), (512, 8), (300, 300), (129, 1000), (1000, 40),
+            (64, 64), (700, 1)]
+    rng = np.random.default_rng(2000 + seed)
+    batch = int(rng.integers(2, 65))
+    picks = rng.integers(0, len(menu), batch)
+    lens_q = [menu[i][0] for i in picks]
+    lens_k = [menu[i][1] for i in picks]
+    lens_q[0], lens_k[0] = 300, 300
+    mask = ("causal", "right_window")[seed % 2]
+    prob = make_problem(f"lf_mix_{seed}", dtype=("f16", "bf16")[seed % 2], lens_q=lens_q,
+                        lens_k=lens_k, hq=8, hkv=2, dqk=(64, 128, 256)[seed % 3],
+                        dv=(64, 128, 256)[seed % 3], seed=seed, varlen_q=True, varlen_k=True,
+                        causal=(mask == "causal"), window=WINDOWS[mask])
+    dev = upload(prob)
+    args = fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                          cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+                          max_seqlen_k=dev["max_seqlen_k"], causal=prob.causal,
+                          window=prob.window, num_kv_splits=1)
+    assert fmha.plan(args).tile_order == 1
+    check(fmha, oracle, prob, splits=(1,), label=mask)
+
+
 def test_tile_table_random_mixes(fmha):
     # the device schedule on many seeded length mixes (tables only, no oracle):
     # sequences with many queries and few keys (cheap but many tiles), the
