@@ -358,6 +358,39 @@ def test_longest_first_random_mixes(fmha, oracle, seed):
     check(fmha, oracle, prob, splits=(1,), label=mask)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_heads_together_random(fmha, oracle, seed):
+    # one query tile per sequence and several splits put the kv heads of one
+    # (sequence, split) together on an XCD (tile order 3, a last partial round
+    # in head pairs): odd and even kv-head counts, GQA, varlen q and k with
+    # empty and short sequences, explicit splits
+    rng = np.random.default_rng(3000 + seed)
+    hkv = (1, 3, 5, 12, 7, 2)[seed]
+    g = (1, 2, 1, 1, 4, 8)[seed]
+    dtype = ("fp8_e4m3", "f16", "bf16")[seed % 3]
+    d = 128 if dtype != "fp8_e4m3" else (128, 192)[seed % 2]
+    rows = 96 if dtype == "fp8_e4m3" else 128  # one query tile: q * g rows at most
+    batch = int(rng.integers(1, 6))
+    lens_q = [int(x) for x in rng.integers(rows // (2 * g), rows // g + 1, batch)]
+    lens_k = [int(x) for x in rng.choice([0, 1, 700, 3000, 5000], size=batch)]
+    lens_k[0] = 4096
+    prob = make_problem(f"heads_together_{seed}", dtype=dtype, lens_q=lens_q, lens_k=lens_k,
+                        hq=hkv * g, hkv=hkv, dqk=d, dv=128, seed=seed, varlen_q=True,
+                        varlen_k=True)
+    dev = upload(prob)
+    splits = (3, 7, 16)[seed % 3]
+    args = fmha.make_args(dev["q"], dev["k"], dev["v"], cu_seqlens_q=dev["cu_seqlens_q"],
+                          cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+                          max_seqlen_k=dev["max_seqlen_k"], num_kv_splits=splits,
+                          q_descale=dev.get("q_descale"), k_descale=dev.get("k_descale"),
+                          v_descale=dev.get("v_descale"))
+    ws = torch.zeros(max(fmha.workspace_size(args), 256), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    pl = fmha.plan(args)
+    assert pl.num_q_tiles == 1 and pl.num_splits == splits and pl.tile_order == 3, pl
+    check(fmha, oracle, prob, splits=(splits,), label=f"hkv={hkv} g={g}")
+
+
 def test_tile_table_random_mixes(fmha):
     # the device schedule on many seeded length mixes (tables only, no oracle):
     # sequences with many queries and few keys (cheap but many tiles), the
