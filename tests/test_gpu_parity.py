@@ -814,6 +814,55 @@ def _f8_args(fmha, dev, out, lse, splits, ws=None):
     return a
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_in_kernel_combine_random(fmha, oracle, seed):
+    # the in-launch combine beyond the fp8 prefix: f16/bf16/fp8 multi-row
+    # kernels, varlen q and k (empty and short sequences, splits that some
+    # sequences do not reach), GQA, 2-12 kv heads, 2-20 splits, causal or not
+    rng = np.random.default_rng(4000 + seed)
+    dtype = ("f16", "bf16", "fp8_e4m3", "f16")[seed]
+    hkv, g = ((2, 4), (5, 1), (3, 2), (12, 1))[seed]
+    splits = (2, 7, 20, 9)[seed]
+    d = 128
+    rows = 96 if dtype == "fp8_e4m3" else 128
+    batch = int(rng.integers(1, 4))
+    # more than 80 query rows per (sequence, kv head) for the f16/bf16 multi-row
+    # kernel (fewer take the 16-row kernel, which has no in-launch combine)
+    lens_q = [int(x) for x in rng.integers(2 * rows // (3 * g) + 1, rows // g + 1, batch)]
+    lens_k = [int(x) for x in rng.choice([0, 1, 900, 2500], size=batch)]
+    lens_k[0] = 3000
+    causal = seed % 2 == 1
+    splits = min(splits, fmha.device_num_cus() // (batch * hkv))  # the grid must be resident
+    prob = make_problem(f"in_kernel_combine_{seed}", dtype=dtype, lens_q=lens_q, lens_k=lens_k,
+                        hq=hkv * g, hkv=hkv, dqk=d, dv=d, seed=seed, varlen_q=True,
+                        varlen_k=True, causal=causal)
+    dev = upload(prob)
+    out, lse = alloc_outputs(prob, dev)
+    args = fmha.make_args(dev["q"], dev["k"], dev["v"], out=out, lse=lse,
+                          cu_seqlens_q=dev["cu_seqlens_q"],
+                          cu_seqlens_k=dev["cu_seqlens_k"], max_seqlen_q=dev["max_seqlen_q"],
+                          max_seqlen_k=dev["max_seqlen_k"], causal=causal, num_kv_splits=splits,
+                          q_descale=dev.get("q_descale"), k_descale=dev.get("k_descale"),
+                          v_descale=dev.get("v_descale"), num_cus=fmha.device_num_cus(),
+                          combine_in_kernel=True)
+    ws = torch.zeros(max(fmha.workspace_size(args), 256), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    pl = fmha.plan(args)
+    assert pl.combine_in_kernel == 1 and pl.num_splits == splits, pl
+    ref = run_oracle(oracle, prob)
+    for rep in range(2):  # the counters are zero again after each launch
+        announce(f"in-kernel combine {dtype} hkv={hkv} g={g} S={splits} causal={causal} rep {rep}")
+        out, lse = alloc_outputs(prob, dev)
+        args.out, args.lse = out.data_ptr(), lse.data_ptr()
+        stream = torch.cuda.current_stream().cuda_stream
+        assert fmha.lib.fmha_fwd(ctypes.byref(args), ctypes.c_void_p(stream)) == 0
+        torch.cuda.synchronize()
+        go, gl = to_packed(prob, out, lse)
+        compare(prob, go, gl, *ref, what=f"in-kernel combine random {seed} rep {rep}")
+    cb = ws[pl.counter_offset:pl.counter_offset + pl.counter_bytes]
+    assert int(cb.count_nonzero()) == 0
+
+
 def test_in_kernel_combine_matches_two_launches(fmha, oracle):
     # fp8 short prefix (12 kv heads, one query tile): with one round of split
     # workgroups fmha_fwd combines inside the attention launch; the result
