@@ -43,15 +43,18 @@ const FwdKernel* registry_bf16_decode(int* n) {
 
 // Prefill instances (32x32 MFMA tiles, 4 waves x 32 rows; key blocks of 32
 // keys for D = 128 and 256 and 64 keys for D = 64: 8 KiB of K or V per block,
-// 16 KiB for D = 256).  Two workgroups share a CU, so the two waves on a SIMD
-// belong to different workgroups and drift out of phase (one on MFMA while the
-// other is on VALU); D = 256 runs one workgroup per CU (its rings take 128 KiB).
+// 16 KiB for D = 256).  D = 64 and 128 run three workgroups per CU on
+// three-stage rings (S3: three waves per SIMD from different workgroups, QK,
+// softmax and PV of a block in turn); D = 256 runs one workgroup per CU (its
+// four-stage rings take 128 KiB) with the cross-block software pipeline.
 #define FMHA_PF(D, NWM, BN, ID) \
   {DT_BF16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_BF16, D, NWM, BN, 1>>}
+#define FMHA_PF3(D, BN, ID) \
+  {DT_BF16, D, D, 4, 1, BN, ID, &launch_prefill<PfCfg<DT_BF16, D, 4, BN, 1, false, true>>}
 
 static const FwdKernel kPfTable[] = {
-    FMHA_PF(64, 4, 64, 200),
-    FMHA_PF(128, 4, 32, 201),
+    FMHA_PF3(64, 64, 200),
+    FMHA_PF3(128, 32, 201),
     FMHA_PF(256, 4, 32, 202),
 };
 

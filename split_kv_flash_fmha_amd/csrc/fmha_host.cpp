@@ -359,11 +359,11 @@ int resolve(const fmha_fwd_args* a, Mode mode, Resolved* r) {
       const int64_t positions = 8 * per_xcd;  // < 2^30 (table entries pack the tile in 20 bits)
       pl.tile_order = kTileOrderTable;
       pl.grid_main = positions;
-      // persistent: one round of workgroups (two per CU, one at head dim 256)
+      // persistent: one round of workgroups (three per CU, one at head dim 256)
       // takes the positions from the table (f16/bf16 prefill kernel)
       if (a->persistent && a->in_dtype != FMHA_DTYPE_FP8_E4M3) {
         pl.persistent = 1;
-        const int64_t round = (int64_t)num_cus * (kern->dqk >= 256 ? 1 : 2);
+        const int64_t round = (int64_t)num_cus * (kern->dqk >= 256 ? 1 : 3);
         pl.grid_main = positions < round ? positions : round;
       }
       pl.sched_offset = 0;

@@ -496,7 +496,7 @@ def test_persistent_table_order_grid():
         a.persistent = persistent
         return check(a)
     st, p = plan(128)
-    assert st == OK and p.tile_order == 4 and p.persistent == 1 and p.grid_main == 512
+    assert st == OK and p.tile_order == 4 and p.persistent == 1 and p.grid_main == 768
     st, p = plan(256)
     assert st == OK and p.persistent == 1 and p.grid_main == 256
     st, p = plan(128, persistent=0)
