@@ -50,7 +50,7 @@ const FwdKernel* registry_f16_decode(int* n) {
 #define FMHA_PF(D, NWM, BN, ID) \
   {DT_F16, D, D, NWM, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, NWM, BN, 1>>}
 #define FMHA_PF3(D, BN, ID) \
-  {DT_F16, D, D, 4, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, 4, BN, 1, false, true>>}
+  {DT_F16, D, D, 4, 1, BN, ID, &launch_prefill<PfCfg<DT_F16, D, 4, BN, 1, false, 3>>}
 
 static const FwdKernel kPfTable[] = {
     FMHA_PF3(64, 64, 200),

@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t pack2_p(float a, float b) {
   return pack2_in<DT>(a, b);
 }
 
-template <int DT_, int D_, int NWM_, int BN_, int RT_, bool PP_ = false, bool S3_ = false>
+template <int DT_, int D_, int NWM_, int BN_, int RT_, bool PP_ = false, int WGS_ = 0>
 struct PfCfg {
   static constexpr int DT = DT_;
   static constexpr int D = D_;          // Dqk == Dv
@@ -98,20 +98,22 @@ struct PfCfg {
   static constexpr int RPL = 1024 / ROWB;          // rows per 1 KiB direct-to-LDS load
   static constexpr int TILE = BN * ROWB;           // one K or V block in LDS
   static constexpr int KL = TILE / 1024 / NWM;     // 1 KiB loads per wave per K (or V) block
-  // S3: three workgroups per CU (a third wave per SIMD) on three-stage rings,
-  // without the cross-block software pipeline (QK, softmax and PV of one
-  // block in turn; the other waves of the SIMD fill the gaps)
-  static constexpr bool S3 = S3_;
-  static constexpr int NS = S3 ? 3 : 4;            // ring depth, K and V each
+  // WGS > 0: the simple loop form with WGS workgroups per CU (WGS waves per
+  // SIMD) on NS-stage rings, without the cross-block software pipeline (QK,
+  // softmax and PV of one block in turn; the other waves of the SIMD fill
+  // the gaps); 0: the pipelined form on four-stage rings
+  static constexpr int WGS = WGS_;
+  static constexpr bool S3 = WGS > 0;              // the simple loop form
+  static constexpr int NS = WGS == 0 ? 4 : (WGS >= 3 ? 3 : 2);  // ring depth, K and V each
   static constexpr int LDS = 2 * NS * TILE;
   // two waves per SIMD (one for RT = 2, or when two rings do not fit the
   // 160 KiB of LDS: D = 256 runs one wave per SIMD with all 512 registers)
-  static constexpr int MIN_BLOCKS = S3 ? 3 : 2 * LDS > 160 * 1024 ? 1 : (RT == 1 ? 8 : 4) / NWM;
+  static constexpr int MIN_BLOCKS = S3 ? WGS : 2 * LDS > 160 * 1024 ? 1 : (RT == 1 ? 8 : 4) / NWM;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
   static_assert(1024 % ROWB == 0 && KL >= 1 && KL * NWM * 1024 == TILE, "whole 1 KiB loads per wave");
   static_assert(TILE % 256 == 0, "stage offsets keep the low address bits");
   static_assert(!PP || (NWM % 2 == 0 && ROWB != 512), "two equal groups; loads issued in one burst");
-  static_assert(!S3 || (!PP && ROWB != 512 && 3 * LDS <= 160 * 1024), "three rings per CU");
+  static_assert(!S3 || (!PP && WGS * LDS <= 160 * 1024), "WGS rings per CU");
 };
 
 // 16-byte chunk c of row r sits at chunk slot c ^ swz(r) (an XOR on the low
@@ -714,18 +716,19 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
     }
   };
 
-  // Three-stage form: iteration it waits for K(it), V(it) (issued two
-  // iterations back), takes the barrier (every wave is done with stage
-  // (it+2)%3 = (it-1)%3), issues K(it+2), V(it+2) there, then runs QK(it),
-  // the softmax of block it and PV(it).
+  // Simple form on NS-stage rings: iteration it waits for K(it), V(it)
+  // (issued NS-1 iterations back), takes the barrier (every wave is done with
+  // stage (it+NS-1)%NS = (it-1)%NS), issues K(it+NS-1), V(it+NS-1) there,
+  // then runs QK(it), the softmax of block it and PV(it).
+  constexpr int NS = C::NS;
   auto body3 = [&](auto ST_, auto FIRST_, int it) {
     constexpr int ST = decltype(ST_)::value;
     constexpr bool FIRST = decltype(FIRST_)::value != 0;
     const int j0 = j_begin + it * C::BN;
-    wait_loads(int_c<2 * C::KL>{});
+    wait_loads(int_c<(NS - 2) * 2 * C::KL>{});
     block_barrier();
-    issue_k(j0 + 2 * C::BN, int_c<(ST + 2) % 3>{});
-    issue_v(j0 + 2 * C::BN, int_c<(ST + 2) % 3>{});
+    issue_k(j0 + (NS - 1) * C::BN, int_c<(ST + NS - 1) % NS>{});
+    issue_v(j0 + (NS - 1) * C::BN, int_c<(ST + NS - 1) % NS>{});
     f32x16 (&s)[RT][C::NT] = sbuf[0];
     u32x4 (&pc)[RT][C::NG] = pbuf[0];
     qk(int_c<ST>{}, s, nothing);
@@ -776,19 +779,22 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
   };
   if constexpr (C::S3) {
     if (n_iter > 0) {
-      issue_k(j_begin, int_c<0>{});
-      issue_v(j_begin, int_c<0>{});
-      issue_k(j_begin + C::BN, int_c<1>{});
-      issue_v(j_begin + C::BN, int_c<1>{});
+      static_for<NS - 1>([&](auto I_) {
+        constexpr int i = decltype(I_)::value;
+        issue_k(j_begin + i * C::BN, int_c<i>{});
+        issue_v(j_begin + i * C::BN, int_c<i>{});
+      });
       body3(int_c<0>{}, int_c<1>{}, 0);
       int it = 1;
       for (;;) {
         if (it >= n_iter) break;
-        body3(int_c<1>{}, int_c<0>{}, it++);
+        body3(int_c<1 % NS>{}, int_c<0>{}, it++);
         if (it >= n_iter) break;
-        body3(int_c<2>{}, int_c<0>{}, it++);
-        if (it >= n_iter) break;
-        body3(int_c<0>{}, int_c<0>{}, it++);
+        body3(int_c<2 % NS>{}, int_c<0>{}, it++);
+        if constexpr (NS == 3) {
+          if (it >= n_iter) break;
+          body3(int_c<0>{}, int_c<0>{}, it++);
+        }
       }
       // every load of the ring retires before the workgroup's LDS is reused
       __builtin_amdgcn_s_waitcnt(0);
