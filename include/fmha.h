@@ -157,7 +157,9 @@ typedef enum fmha_status {
  *  persistent   : 1 = when the plan sorts its tiles on the device (tile order 4,
  *                 f16/bf16), launch one round of workgroups that take tiles
  *                 from the table until none is left, instead of one workgroup
- *                 per tile; 0 = one workgroup per tile (default).
+ *                 per tile; 0 = one workgroup per tile (default).  Measured on
+ *                 MI355X the default is faster (by 44 % on 128 causal
+ *                 sequences at head dim 128).
  */
 typedef struct fmha_fwd_args {
   const void* q;
