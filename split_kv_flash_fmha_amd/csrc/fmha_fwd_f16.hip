@@ -44,7 +44,7 @@ const FwdKernel* registry_f16_decode(int* n) {
 // Prefill instances (32x32 MFMA tiles, 4 waves x 32 rows; key blocks of 32
 // keys for D = 128 and 256 and 64 keys for D = 64: 8 KiB of K or V per block,
 // 16 KiB for D = 256).  D = 64 and 128 run three workgroups per CU on
-// three-stage rings (S3: three waves per SIMD from different workgroups, QK,
+// three-stage rings (the simple loop form: three waves per SIMD from different workgroups, QK,
 // softmax and PV of a block in turn); D = 256 runs one workgroup per CU (its
 // four-stage rings take 128 KiB) with the cross-block software pipeline.
 #define FMHA_PF(D, NWM, BN, ID) \

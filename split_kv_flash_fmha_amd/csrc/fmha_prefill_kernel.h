@@ -26,7 +26,7 @@
 // of block n, then QK(n+1) on the MFMA pipe while the VALU takes the
 // exponentials of block n; the MFMAs and the VALU work are interleaved in
 // chunks inside each wave, so both pipes stay busy even when the other wave
-// on the SIMD is stalled.  The three-stage one (S3, head dims 64 and 128):
+// on the SIMD is stalled.  The simple one (head dims 64 and 128):
 // three workgroups per CU on three-stage rings, so each SIMD holds three
 // waves of different workgroups, and each wave runs QK(n), the softmax of
 // block n and PV(n) in turn with a single S and P buffer (168 registers or
@@ -103,17 +103,17 @@ struct PfCfg {
   // softmax and PV of one block in turn; the other waves of the SIMD fill
   // the gaps); 0: the pipelined form on four-stage rings
   static constexpr int WGS = WGS_;
-  static constexpr bool S3 = WGS > 0;              // the simple loop form
+  static constexpr bool SIMPLE = WGS > 0;          // the simple loop form
   static constexpr int NS = WGS == 0 ? 4 : (WGS >= 3 ? 3 : 2);  // ring depth, K and V each
   static constexpr int LDS = 2 * NS * TILE;
   // two waves per SIMD (one for RT = 2, or when two rings do not fit the
   // 160 KiB of LDS: D = 256 runs one wave per SIMD with all 512 registers)
-  static constexpr int MIN_BLOCKS = S3 ? WGS : 2 * LDS > 160 * 1024 ? 1 : (RT == 1 ? 8 : 4) / NWM;
+  static constexpr int MIN_BLOCKS = SIMPLE ? WGS : 2 * LDS > 160 * 1024 ? 1 : (RT == 1 ? 8 : 4) / NWM;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile sizes");
   static_assert(1024 % ROWB == 0 && KL >= 1 && KL * NWM * 1024 == TILE, "whole 1 KiB loads per wave");
   static_assert(TILE % 256 == 0, "stage offsets keep the low address bits");
   static_assert(!PP || (NWM % 2 == 0 && ROWB != 512), "two equal groups; loads issued in one burst");
-  static_assert(!S3 || (!PP && WGS * LDS <= 160 * 1024), "WGS rings per CU");
+  static_assert(!SIMPLE || (!PP && WGS * LDS <= 160 * 1024), "WGS rings per CU");
 };
 
 // 16-byte chunk c of row r sits at chunk slot c ^ swz(r) (an XOR on the low
@@ -531,10 +531,10 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
   // the two previous iterations may stay in flight.  The prologue issues in
   // the same order as iterations -4..-1 would (with empty loads for V(-2) and
   // V(-1)), so the count is uniform.
-  static_assert(C::NS == 4 || C::S3, "ring schedule");
+  static_assert(C::NS == 4 || C::SIMPLE, "ring schedule");
   f32x16 sbuf[2][RT][C::NT];  // S of block it in sbuf[it % 2]
   const int jlast = j_begin + n_iter * C::BN;  // first block past the tile's range
-  if constexpr (!C::S3) if (n_iter > 0) {
+  if constexpr (!C::SIMPLE) if (n_iter > 0) {
     issue_k(j_begin, int_c<0>{});
     issue_v(jlast, int_c<2>{});  // empty
     issue_k(j_begin + C::BN, int_c<1>{});
@@ -721,7 +721,7 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
   // stage (it+NS-1)%NS = (it-1)%NS), issues K(it+NS-1), V(it+NS-1) there,
   // then runs QK(it), the softmax of block it and PV(it).
   constexpr int NS = C::NS;
-  auto body3 = [&](auto ST_, auto FIRST_, int it) {
+  auto body_simple = [&](auto ST_, auto FIRST_, int it) {
     constexpr int ST = decltype(ST_)::value;
     constexpr bool FIRST = decltype(FIRST_)::value != 0;
     const int j0 = j_begin + it * C::BN;
@@ -777,30 +777,30 @@ __device__ __forceinline__ void prefill_tile(const FwdParams& p, const WorkItem&
     }
     pv(int_c<ST>{}, pc, nothing);
   };
-  if constexpr (C::S3) {
+  if constexpr (C::SIMPLE) {
     if (n_iter > 0) {
       static_for<NS - 1>([&](auto I_) {
         constexpr int i = decltype(I_)::value;
         issue_k(j_begin + i * C::BN, int_c<i>{});
         issue_v(j_begin + i * C::BN, int_c<i>{});
       });
-      body3(int_c<0>{}, int_c<1>{}, 0);
+      body_simple(int_c<0>{}, int_c<1>{}, 0);
       int it = 1;
       for (;;) {
         if (it >= n_iter) break;
-        body3(int_c<1 % NS>{}, int_c<0>{}, it++);
+        body_simple(int_c<1 % NS>{}, int_c<0>{}, it++);
         if (it >= n_iter) break;
-        body3(int_c<2 % NS>{}, int_c<0>{}, it++);
+        body_simple(int_c<2 % NS>{}, int_c<0>{}, it++);
         if constexpr (NS == 3) {
           if (it >= n_iter) break;
-          body3(int_c<0>{}, int_c<0>{}, it++);
+          body_simple(int_c<0>{}, int_c<0>{}, it++);
         }
       }
       // every load of the ring retires before the workgroup's LDS is reused
       __builtin_amdgcn_s_waitcnt(0);
     }
   }
-  if constexpr (!C::S3) if (n_iter > 0) {
+  if constexpr (!C::SIMPLE) if (n_iter > 0) {
     // group 1 of the two-group variant: one barrier of delay (its loads up to
     // K(1) landed first: group 0's first MFMA phase reads K(1))
     if (pp_late) {
